@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every check here is independent of the oracle's own code path: page worked
+examples (tests/golden), closed forms, library routines the method reduces to,
+brute force over tiny inputs, and invariants.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from conftest import GOLDEN
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- page examples
+def test_ep47_worked_examples():
+    g = _load("ep47_ledger_cases.json")
+    for case in g["cases"]:
+        s = O.summarize_routes(case["routes"], case["num_experts"], case["hidden_size"],
+                               case["bytes_per_elem"], case["capacity_factor"])
+        for key, want in case["expect"].items():
+            if key == "balance_ratio_3dp":
+                assert round(s["balance_ratio"], 3) == want, case["name"]
+            elif key == "balance_ratio_gt":
+                assert s["balance_ratio"] > want, case["name"]
+            else:
+                assert s[key] == want, (case["name"], key, s[key], want)
+        assert s["all_to_all_bytes"] == 2 * s["dispatch_bytes"]
+
+
+def test_ep46_contracts():
+    g = _load("ep46_contract_cases.json")
+    c = g["capacity"]
+    s = O.summarize_routes(c["routes"], c["num_experts"], c["hidden_size"])
+    for key, want in c["expect"].items():
+        if key == "balance_ratio_3dp":
+            assert round(s["balance_ratio"], 3) == want
+        else:
+            assert s[key] == want, key
+    e = g["empty"]
+    s = O.summarize_routes(e["routes"], e["num_experts"], e["hidden_size"])
+    for key, want in e["expect"].items():
+        assert s[key] == want
+    assert s["balance_ratio"] == 0.0
+    for bad in g["invalid"]:
+        with pytest.raises(ValueError):
+            O.summarize_routes(bad["routes"], bad["num_experts"], bad["hidden_size"])
+    tt = g["two_token_capacity"]
+    s = O.summarize_routes(tt["routes"], tt["num_experts"], tt["hidden_size"])
+    assert s["overflow"] == tt["expect"]["overflow"]
+    assert s["balance_ratio"] <= tt["expect"]["balance_ratio_le"]
+    loc = g["locality"]
+    owners = {int(k): v for k, v in loc["expert_owner_ranks"].items()}
+    d = O.dispatch_locality(loc["routes"], loc["token_source_ranks"], owners,
+                            loc["hidden_size"], loc["bytes_per_elem"])
+    assert d == loc["expect"]
+    with pytest.raises(ValueError):
+        O.dispatch_locality([[0]], [0, 1], owners, 8)
+    with pytest.raises(ValueError):
+        O.dispatch_locality([[2]], [0], owners, 8)
+    cb = g["combine"]
+    out = O.combine_index_add(cb["token_indices"], cb["expert_outputs"],
+                              cb["routing_weights"], cb["num_tokens"])
+    np.testing.assert_allclose(out, np.asarray(cb["expect"]), rtol=0, atol=1e-12)
+
+
+def test_capacity_rounds_up():
+    # 11 routes on 2 experts at cf 1.0: 5.5 -> 6 (the page's rejected case)
+    assert O.capacity(11, 2, 1.0) == 6
+    assert O.capacity(0, 4, 1.25) == 0
+    assert O.capacity(2048, 16, 1.25) == 160
+    assert O.capacity(8192, 8, 1.25) == 1280
+    assert O.capacity(32768, 256, 1.0) == 128
+    assert O.capacity(98304, 64, 1.0) == 1536
+    assert O.capacity(128, 4, 1.0) == 32
+    assert O.capacity(3, 2, 1.0) == 2
+    assert O.capacity(1, 3, 0.5) == 1
+    for bad in [(4, 0, 1.0), (4, 2, 0.0), (4, 2, -1.0), (4, 2, float("nan"))]:
+        with pytest.raises(ValueError):
+            O.capacity(*bad)
+
+
+def test_epc_pair_bytes_table():
+    g = _load("epc_pair_bytes.json")
+    rng = np.random.default_rng(0)
+    for c in g["cases"]:
+        # any routing of B tokens with K experts each has A = B*K routes
+        T, K, h, n = c["B"], c["K"], c["h"], c["N_EP"]
+        E = 256 if c["model"] == "DeepSeek-V3" else 16
+        idx = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+        s = O.summarize_routes(O.routes_from_idx(idx), E, h, c["dtype_bytes"])
+        per_pair = s["logical_route_bytes"] / n
+        assert per_pair == c["expect_bytes"]
+        if c["compare"].startswith("bytes/1e6"):
+            assert f"{per_pair / 1e6:.1f} MB" == c["page_value"]
+        else:
+            assert f"{per_pair / 2**20:.2f} MB" == c["page_value"]
+
+
+def test_round_robin_placement_example():
+    g = _load("dsv3_placement.json")
+    p = O.uniform_expert_placement(g["num_experts"], g["num_devices"])
+    for dev, experts in g["expect"].items():
+        assert p[int(dev)] == experts
+    assert all(len(v) == g["experts_per_device"] for v in p.values())
+    assert sorted(sum(p.values(), [])) == list(range(g["num_experts"]))
+
+
+# ---------------------------------------------------------------- closed forms
+def test_aux_loss_closed_forms():
+    alpha = 0.01
+    rng = np.random.default_rng(1)
+    # perfectly balanced selections: every expert in exactly T*K/E tokens
+    E, K, T = 8, 2, 64
+    idx = np.array([[(2 * t) % E, (2 * t + 1) % E] for t in range(T)])
+    gate = rng.random((T, K))
+    gate /= gate.sum(1, keepdims=True)
+    a = O.aux_loss_terms(idx, gate, E, alpha)
+    assert np.allclose(a["f"], K / E)
+    assert math.isclose(a["l_aux"], alpha * K / E, rel_tol=1e-12)
+    assert math.isclose(a["l_aux_norm"], alpha, rel_tol=1e-12)
+    assert math.isclose(a["P"].sum(), 1.0, rel_tol=1e-12)
+    # every token on expert 0 with K = 1
+    idx = np.zeros((T, 1), int)
+    a = O.aux_loss_terms(idx, np.ones((T, 1)), E, alpha)
+    assert math.isclose(a["l_aux"], alpha, rel_tol=1e-12)
+    assert math.isclose(a["l_aux_norm"], alpha * E, rel_tol=1e-12)
+    a = O.aux_loss_terms(np.zeros((0, 2), int), np.zeros((0, 2)), E, alpha)
+    assert a["l_aux"] == 0.0 and a["l_aux_norm"] == 0.0
+
+
+def test_round_bf16_special_values_and_torch():
+    one = 1.0
+    assert O.round_bf16(one) == 1.0
+    assert O.round_bf16(1 + 2 ** -8) == 1.0                 # tie -> even (down)
+    assert O.round_bf16(1 + 3 * 2 ** -8) == 1 + 2 ** -6      # tie -> even (up)
+    assert O.round_bf16(1 + 2 ** -8 + 2 ** -30) == 1 + 2 ** -7
+    assert O.round_bf16(-0.0) == 0.0
+    assert O.round_bf16(3.0) == 3.0
+    rng = np.random.default_rng(2)
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_bf16(v.astype(np.float64)), ref)
+    np.testing.assert_array_equal(O.round_f32(np.float64(1 + 2 ** -40)), 1.0)
+
+
+def test_gelu_tanh_matches_torch():
+    u = np.linspace(-8, 8, 4001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(u), approximate="tanh").numpy()
+    np.testing.assert_allclose(O.gelu_tanh(u), ref, rtol=1e-14, atol=1e-15)
+    assert O.gelu_tanh(0.0) == 0.0
+
+
+# ---------------------------------------------------------------- router
+def test_router_logits_exact_integers():
+    rng = np.random.default_rng(3)
+    x = rng.integers(-4, 5, (13, 7)).astype(np.float64)
+    w = rng.integers(-3, 4, (5, 7)).astype(np.float64)
+    got = O.router_logits(x, w)
+    for t in range(13):
+        for e in range(5):
+            assert got[t, e] == sum(int(x[t, j]) * int(w[e, j]) for j in range(7))
+    # W_g acts on x as a column: logits[t] = W_g @ x[t], not W_g^T
+    x = rng.standard_normal((3, 4))
+    w = rng.standard_normal((6, 4))
+    np.testing.assert_allclose(O.router_logits(x, w), (w @ x.T).T.astype(np.float32))
+
+
+def test_topk_softmax_matches_torch_without_ties():
+    rng = np.random.default_rng(4)
+    for E, K in [(4, 2), (16, 1), (8, 2), (64, 6), (256, 8), (5, 5)]:
+        l = rng.standard_normal((50, E)).astype(np.float32)
+        idx, g = O.topk_softmax(l, K)
+        tv, ti = torch.topk(torch.from_numpy(l).double(), K, dim=-1)
+        assert np.array_equal(idx, ti.numpy())
+        ref = torch.softmax(tv, dim=-1).numpy()
+        np.testing.assert_allclose(g, ref.astype(np.float32), rtol=2e-7, atol=0)
+        np.testing.assert_allclose(g.astype(np.float64).sum(1), 1.0, rtol=1e-6)
+        if K == 1:
+            assert np.all(g == 1.0)
+
+
+def test_topk_ties_brute_force():
+    rng = np.random.default_rng(5)
+    for E, K in [(4, 2), (6, 3), (8, 8), (3, 1)]:
+        l = rng.integers(-2, 3, (200, E)).astype(np.float32)
+        l[rng.random(l.shape) < 0.1] = -0.0
+        idx, g = O.topk_softmax(l, K)
+        for t in range(l.shape[0]):
+            # brute force: the K smallest (-logit, id) pairs, in that order
+            pairs = sorted((-float(l[t, e]) + 0.0, e) for e in range(E))
+            assert [e for _, e in pairs[:K]] == list(idx[t])
+            sel = [float(l[t, e]) for e in idx[t]]
+            den = sum(math.exp(v) for v in sel)
+            for k in range(K):
+                assert abs(g[t, k] - math.exp(sel[k]) / den) <= 1e-7 * g[t, k] + 1e-12
+    with pytest.raises(ValueError):
+        O.topk_softmax(np.zeros((2, 3), np.float32), 4)
+
+
+def test_logit_bias_changes_the_routing_and_is_kept_in_the_softmax():
+    l = np.array([[1.0, 0.5, 0.0]], np.float32)
+    b = np.array([0.0, 1.0, 0.0], np.float32)
+    idx, g = O.topk_softmax(l, 2, b)
+    assert list(idx[0]) == [1, 0]
+    e = math.exp(1.5) + math.exp(1.0)
+    assert abs(g[0, 0] - math.exp(1.5) / e) < 1e-7
+
+
+# ---------------------------------------------------------------- slotting
+def _all_routings(T, E, K):
+    per_token = list(itertools.permutations(range(E), K))
+    return itertools.product(per_token, repeat=T)
+
+
+@pytest.mark.parametrize("T,E,K", [(1, 1, 1), (2, 2, 1), (3, 2, 2), (4, 3, 1), (3, 3, 2), (4, 3, 2)])
+def test_slotting_brute_force(T, E, K):
+    A = T * K
+    for routing in _all_routings(T, E, K):
+        idx = np.array(routing, dtype=np.int32).reshape(T, K)
+        flat = idx.reshape(-1)
+        loads = [int((flat == e).sum()) for e in range(E)]
+        for cap in range(0, A + 1):
+            sl = O.slot_routes(idx, E, cap)
+            # independent formulation: rank = earlier routes (row-major) to the same expert
+            rank = np.array([int((flat[:i] == flat[i]).sum()) for i in range(A)]).reshape(T, K)
+            assert np.array_equal(sl["route_rank"], rank)
+            acc = [min(l, cap) for l in loads]
+            off = np.concatenate([[0], np.cumsum(acc)])
+            assert np.array_equal(sl["expert_offsets"], off)
+            want_row = np.where(rank < cap, off[idx] + rank, -1)
+            assert np.array_equal(sl["route_row"], want_row)
+            R = int(off[-1])
+            assert sl["R"] == R and R + O.overflow(loads, cap) == A
+            rows = sorted(int(r) for r in sl["route_row"].reshape(-1) if r >= 0)
+            assert rows == list(range(R))
+            for e in range(E):
+                seg = sl["row_token"][off[e]:off[e + 1]]
+                assert np.all(np.diff(seg) > 0)          # token order inside a segment
+            for t in range(T):
+                for k in range(K):
+                    if sl["route_row"][t, k] >= 0:
+                        assert sl["row_token"][sl["route_row"][t, k]] == t
+
+
+def test_slotting_rejects_bad_ids():
+    with pytest.raises(ValueError):
+        O.slot_routes(np.array([[3]]), 3, 1)
+    with pytest.raises(ValueError):
+        O.expert_loads(np.array([[-1]]), 3)
+
+
+# ---------------------------------------------------------------- FFN, combine, layer
+def test_expert_ffn_matches_torch_linear_gelu():
+    rng = np.random.default_rng(6)
+    E, F, h = 3, 12, 5
+    w1 = rng.standard_normal((E, F, h)); b1 = rng.standard_normal((E, F))
+    w2 = rng.standard_normal((E, h, F)); b2 = rng.standard_normal((E, h))
+    offsets = np.array([0, 4, 4, 9])
+    xd = rng.standard_normal((9, h))
+    H, Y = O.expert_ffn(xd, offsets, w1, b1, w2, b2)
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        a = torch.from_numpy(xd[lo:hi])
+        hh = torch.nn.functional.gelu(torch.nn.functional.linear(a, torch.from_numpy(w1[e]),
+                                                                 torch.from_numpy(b1[e])),
+                                      approximate="tanh")
+        y = torch.nn.functional.linear(hh, torch.from_numpy(w2[e]), torch.from_numpy(b2[e]))
+        np.testing.assert_allclose(H[lo:hi], hh.numpy(), rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(Y[lo:hi], y.numpy().astype(np.float32), rtol=1e-6, atol=1e-6)
+    # sampled-row form agrees with the segment form
+    rows_e = np.array([0, 0, 2, 2, 2, 0])
+    rows = np.array([0, 3, 4, 8, 5, 1])
+    H2, Y2 = O.expert_ffn_rows(xd[rows], rows_e, w1, b1, w2, b2)
+    np.testing.assert_allclose(Y2, Y[rows], rtol=1e-6, atol=1e-7)
+    # bf16 rounding of H moves it to the bf16 grid
+    Hb, _ = O.expert_ffn(xd, offsets, w1, b1, w2, b2, h_round="bf16")
+    assert np.array_equal(Hb, O.round_bf16(Hb))
+    assert np.max(np.abs(Hb - H)) <= np.max(np.abs(H)) * 2 ** -8
+
+
+def test_combine_gather_equals_index_add():
+    rng = np.random.default_rng(7)
+    T, K, h, R = 20, 3, 6, 70
+    Y = rng.standard_normal((R, h)).astype(np.float32)
+    gate = rng.random((T, K)).astype(np.float32)
+    rows = rng.permutation(R)[:T * K].reshape(T, K).astype(np.int32)
+    rows[rng.random((T, K)) < 0.3] = -1
+    rows[0, :] = -1                                  # a token with every route dropped
+    out = O.combine(Y, rows, gate)
+    m = rows.reshape(-1) >= 0
+    tok = np.repeat(np.arange(T), K)[m]
+    ref = O.combine_index_add(tok, Y[rows.reshape(-1)[m]], gate.reshape(-1)[m], T)
+    np.testing.assert_allclose(out, ref.astype(np.float32), rtol=1e-6, atol=1e-7)
+    assert np.all(out[0] == 0.0)
+
+
+def _small_layer(T=40, h=16, E=5, K=2, F=24, seed=8):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, h))
+    wg = rng.standard_normal((E, h)) / math.sqrt(h)
+    w1 = rng.standard_normal((E, F, h)) / math.sqrt(h)
+    b1 = 0.1 * rng.standard_normal((E, F))
+    w2 = rng.standard_normal((E, h, F)) / math.sqrt(F)
+    b2 = 0.1 * rng.standard_normal((E, h))
+    return x, wg, w1, b1, w2, b2
+
+
+@pytest.mark.parametrize("cf", [0.5, 1.0, 1e9])
+def test_layer_two_formulations_agree(cf):
+    x, wg, w1, b1, w2, b2 = _small_layer()
+    K = 2
+    L = O.moe_layer(x, wg, w1, b1, w2, b2, K, cf)
+    acc = L["route_row"] >= 0
+    out2 = O.moe_layer_per_token(x, L["idx"], L["gate"], acc, w1, b1, w2, b2)
+    np.testing.assert_allclose(L["out"], out2, rtol=1e-6, atol=1e-7)
+    if cf == 1e9:
+        assert acc.all()
+        # with nothing dropped the layer is the dense top-k MoE: sum_k g_k FFN_k(x)
+        xt = torch.from_numpy(x)
+        dense = torch.zeros_like(xt)
+        for t in range(x.shape[0]):
+            for k in range(K):
+                e = int(L["idx"][t, k])
+                hh = torch.nn.functional.gelu(xt[t] @ torch.from_numpy(w1[e]).T
+                                              + torch.from_numpy(b1[e]), approximate="tanh")
+                dense[t] += float(L["gate"][t, k]) * (hh @ torch.from_numpy(w2[e]).T
+                                                      + torch.from_numpy(b2[e]))
+        np.testing.assert_allclose(L["out"], dense.numpy(), rtol=1e-5, atol=1e-6)
+    else:
+        assert (~acc).any()
+
+
+def test_ledger_invariants_and_empty():
+    x, wg, w1, b1, w2, b2 = _small_layer(T=64, E=6, K=2)
+    L = O.moe_layer(x, wg, w1, b1, w2, b2, 2, 0.8)
+    src = np.arange(64) % 3
+    owner = np.arange(6) % 3
+    led = O.ledger(L["idx"], L["gate"], L["route_row"], L["capacity"], src, owner, 3, 16, 2)
+    A = 128
+    assert led["total_routes"] == A and int(led["expert_loads"].sum()) == A
+    assert led["local_routes"] + led["cross_rank_routes"] == A
+    assert led["all_to_all_bytes"] == 2 * led["dispatch_bytes"]
+    assert led["accepted_routes"] + led["overflow"] == A
+    assert led["accepted_local_routes"] + led["accepted_cross_rank_routes"] == led["accepted_routes"]
+    assert int(led["pair_routes"].sum()) == led["accepted_routes"]
+    assert int(np.trace(led["pair_routes"])) == led["accepted_local_routes"]
+    assert math.isclose(led["f"].sum(), 2.0, rel_tol=1e-12)
+    assert math.isclose(led["P"].sum(), 1.0, rel_tol=1e-6)
+    assert led["local_hit_ratio"] == led["local_routes"] / A
+    assert led["cross_rank_roundtrip_bytes"] == 2 * led["cross_rank_dispatch_bytes"]
+    assert led["balance_ratio"] == led["max_load"] / (A / 6)
+    # empty batch: zero ledger
+    z = O.ledger(np.zeros((0, 2), np.int32), np.zeros((0, 2), np.float32),
+                 np.zeros((0, 2), np.int32), 0, np.zeros(0, int), owner, 3, 16, 2)
+    assert z["total_routes"] == 0 and z["capacity"] == 0 and z["balance_ratio"] == 0.0
+    assert z["local_hit_ratio"] == 0.0 and z["l_aux"] == 0.0
+    with pytest.raises(ValueError):
+        O.ledger(L["idx"], L["gate"], L["route_row"], 1, src, np.arange(6) % 4, 3, 16, 2)
+
+
+def test_load_monitor_alarm():
+    m = O.load_monitor([10, 1])
+    assert math.isclose(m["max_over_mean"], 10 / 5.5)
+    assert not m["imbalanced"]
+    m = O.load_monitor([30, 1, 1, 0])
+    assert m["imbalanced"]
+    assert math.isclose(m["var_over_mean"], float(np.var([30, 1, 1, 0], ddof=1)) / 8.0)
