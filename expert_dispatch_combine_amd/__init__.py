@@ -1,0 +1,22 @@
+"""expert_dispatch_combine_amd: one MoE layer hot path on an MI355X (gfx950).
+
+route -> capacity-limited dispatch -> expert FFN -> weighted combine, plus a
+counters-only ledger, implemented as hand-written HIP kernels behind the C ABI
+of include/moe.h (libmoe.so).  This module is the thin Python binding: it only
+marshals torch tensors (device memory) and the current HIP stream into the C
+calls, which have the same names.  Every step of the path runs in the library;
+there is no fallback: if libmoe.so is missing or fails to load, every call
+raises.
+"""
+from ._binding import (  # noqa: F401
+    MOE_BF16, MOE_F32, MoeCfg, MoeError, MoeLedger, library_path, load_library,
+    moe_capacity, moe_combine, moe_dispatch, moe_expert_ffn, moe_ledger, moe_max_rows,
+    moe_route, moe_status_string, moe_workspace_bytes, EXPORTED_SYMBOLS,
+)
+
+__all__ = [
+    "MOE_BF16", "MOE_F32", "MoeCfg", "MoeError", "MoeLedger", "library_path", "load_library",
+    "moe_capacity", "moe_combine", "moe_dispatch", "moe_expert_ffn", "moe_ledger",
+    "moe_max_rows", "moe_route", "moe_status_string", "moe_workspace_bytes",
+    "EXPORTED_SYMBOLS",
+]

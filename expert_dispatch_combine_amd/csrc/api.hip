@@ -1,0 +1,269 @@
+// C-ABI layer of libmoe: argument validation, workspace carving, kernel
+// launches on the caller's stream, and the ledger's host-side float64 math.
+// Declarations and contracts are in include/moe.h.
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "moe.h"
+#include "moe_internal.hpp"
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_cfg(const moe_cfg* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->h <= 0 || c->E <= 0 || c->K <= 0 || c->F <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->K > c->E) return MOE_ERR_INVALID_ARG;
+  if (!(c->capacity_factor > 0.0) || !std::isfinite(c->capacity_factor))
+    return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->E > kMaxExperts || c->K > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)c->T * c->K > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (c->dtype == MOE_BF16 && (c->h % 64 != 0 || c->F % 64 != 0)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t routes_of(const moe_cfg* c) { return (int64_t)c->T * c->K; }
+
+int64_t rows_max(const moe_cfg* c, int64_t cap) {
+  const int64_t A = routes_of(c);
+  const int64_t ecap = (int64_t)c->E * cap;
+  return A < ecap ? A : ecap;
+}
+
+int elem_bytes(const moe_cfg* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_EXPERT_ID: return "MOE_ERR_EXPERT_ID";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+int64_t moe_capacity(int64_t A, int32_t E, double capacity_factor) {
+  if (E <= 0 || A < 0 || !(capacity_factor > 0.0) || !std::isfinite(capacity_factor))
+    return -1;
+  if (A == 0) return 0;
+  const double v = std::ceil(((double)A / (double)E) * capacity_factor);
+  if (!(v < 9.0e18)) return -1;
+  return (int64_t)v;
+}
+
+int64_t moe_max_rows(const moe_cfg* cfg, int64_t capacity) {
+  if (check_cfg(cfg) != MOE_OK || capacity < 0) return -1;
+  return rows_max(cfg, capacity);
+}
+
+size_t moe_workspace_bytes(const moe_cfg* cfg) {
+  if (check_cfg(cfg) != MOE_OK) return 0;
+  const int64_t A = routes_of(cfg);
+  size_t a = dispatch_ws_bytes(A, cfg->E);
+  size_t b = ledger_ws_bytes(A, cfg->E, kMaxRanks);
+  return (a > b ? a : b) + 256;
+}
+
+int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate, const float* logit_bias,
+              float* logits, int32_t* topk_idx, float* topk_gate, int32_t* expert_load,
+              void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int T = cfg->T, h = cfg->h, E = cfg->E, K = cfg->K;
+  if (T > 0 && (!logits || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
+  if (x && !w_gate) return MOE_ERR_INVALID_ARG;
+  if (expert_load) {
+    st = hip_status(launch_zero_i32(expert_load, E, s));
+    if (st != MOE_OK) return st;
+  }
+  if (T == 0) return MOE_OK;
+  if (x) {
+    if (cfg->dtype == MOE_BF16) {
+      if (!aligned16(x) || !aligned16(w_gate)) return MOE_ERR_INVALID_ARG;
+      if (E <= 64 && K <= 16)
+        return hip_status(launch_router_topk_bf16((const uint16_t*)x, (const uint16_t*)w_gate,
+                                                  logit_bias, logits, topk_idx, topk_gate,
+                                                  expert_load, T, h, E, K, s));
+      st = hip_status(launch_router_gemm_bf16((const uint16_t*)x, (const uint16_t*)w_gate,
+                                              logits, T, h, E, s));
+    } else {
+      st = hip_status(launch_router_gemm_f32((const float*)x, (const float*)w_gate, logits, T,
+                                             h, E, s));
+    }
+    if (st != MOE_OK) return st;
+  }
+  return hip_status(
+      launch_topk_softmax(logits, logit_bias, topk_idx, topk_gate, expert_load, T, E, K, s));
+}
+
+int moe_dispatch(const moe_cfg* cfg, const void* x, const int32_t* topk_idx, int64_t capacity,
+                 int32_t* expert_offsets, int32_t* route_rank, int32_t* route_row,
+                 int32_t* row_token, void* x_disp, int32_t* expert_load, void* ws,
+                 size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  const int64_t A = routes_of(cfg);
+  const int64_t rmax = rows_max(cfg, capacity);
+  if (!expert_offsets || !ws) return MOE_ERR_INVALID_ARG;
+  if (A > 0 && (!topk_idx || !route_rank || !route_row)) return MOE_ERR_INVALID_ARG;
+  if (rmax > 0 && (!x || !x_disp || !row_token)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe_workspace_bytes(cfg)) return MOE_ERR_SHAPE;
+  const int64_t row_bytes = (int64_t)cfg->h * elem_bytes(cfg);
+  return hip_status(launch_dispatch(x, topk_idx, A, cfg->K, cfg->E, capacity, row_bytes, rmax,
+                                    expert_offsets, route_rank, route_row, row_token, x_disp,
+                                    expert_load, ws, (hipStream_t)stream));
+}
+
+int moe_expert_ffn(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
+                   const int32_t* expert_offsets, const void* w1, const float* b1,
+                   const void* w2, const float* b2, void* h_buf, float* y, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  const int64_t rmax = rows_max(cfg, capacity);
+  if (rmax == 0) return MOE_OK;
+  if (!x_disp || !expert_offsets || !w1 || !b1 || !w2 || !b2 || !h_buf || !y)
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (cfg->dtype == MOE_BF16) {
+    if (!aligned16(x_disp) || !aligned16(w1) || !aligned16(w2) || !aligned16(h_buf) ||
+        !aligned16(y) || !aligned16(b1) || !aligned16(b2))
+      return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_ffn_bf16((const uint16_t*)x_disp, expert_offsets,
+                                      (const uint16_t*)w1, b1, (const uint16_t*)w2, b2,
+                                      (uint16_t*)h_buf, y, cfg->E, cfg->h, cfg->F, rmax, s));
+  }
+  return hip_status(launch_ffn_f32((const float*)x_disp, expert_offsets, (const float*)w1, b1,
+                                   (const float*)w2, b2, (float*)h_buf, y, cfg->E, cfg->h,
+                                   cfg->F, rmax, s));
+}
+
+int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* route_row,
+                const float* topk_gate, float* out, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!route_row || !topk_gate || !out) return MOE_ERR_INVALID_ARG;
+  // y may be NULL only when nothing was accepted; the kernel never reads it then
+  return hip_status(launch_combine(y, route_row, topk_gate, out, cfg->T, cfg->K, cfg->h,
+                                   (hipStream_t)stream));
+}
+
+int moe_ledger(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_gate,
+               const int32_t* route_row, int64_t capacity, const int32_t* src_rank,
+               const int32_t* owner_rank, int32_t n_ep, double alpha, moe_ledger_t* out,
+               int64_t* loads, double* f, double* P, int64_t* pair_routes, void* ws,
+               size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!out || !owner_rank || !ws || capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (n_ep < 1 || n_ep > kMaxRanks) return MOE_ERR_INVALID_ARG;
+  const int T = cfg->T, K = cfg->K, E = cfg->E;
+  if (T > 0 && (!topk_idx || !topk_gate || !route_row || !src_rank)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe_workspace_bytes(cfg)) return MOE_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  void* fin = nullptr;
+  size_t fin_bytes = 0;
+  st = hip_status(launch_ledger(topk_idx, topk_gate, route_row, src_rank, owner_rank, T, K, E,
+                                n_ep, ws, &fin, &fin_bytes, s));
+  if (st != MOE_OK) return st;
+  std::vector<char> host(fin_bytes);
+  if (hipMemcpyAsync(host.data(), fin, fin_bytes, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+  const int64_t* h_load = (const int64_t*)host.data();
+  const double* h_P = (const double*)(host.data() + (size_t)E * 8);
+  const int64_t* h_cnt = (const int64_t*)(host.data() + (size_t)2 * E * 8);
+  const int64_t* h_pair = (const int64_t*)(host.data() + (size_t)(2 * E + LC_N) * 8);
+
+  const int64_t A = routes_of(cfg);
+  const int64_t be = elem_bytes(cfg);
+  const int64_t hsz = cfg->h;
+  moe_ledger_t L;
+  std::memset(&L, 0, sizeof(L));
+  L.total_tokens = T;
+  L.total_routes = A;
+  L.num_experts = E;
+  L.capacity = capacity;
+  L.n_ep = n_ep;
+  L.alpha = alpha;
+  int64_t max_load = 0, ovf = 0, sum_load = 0;
+  for (int e = 0; e < E; ++e) {
+    const int64_t l = h_load[e];
+    if (l > max_load) max_load = l;
+    if (l > capacity) ovf += l - capacity;
+    sum_load += l;
+  }
+  L.max_load = max_load;
+  L.overflow = ovf;
+  L.accepted_routes = h_cnt[LC_ACCEPTED];
+  L.invalid_routes = h_cnt[LC_INVALID_ID];
+  L.logical_route_bytes = A * hsz * be;
+  L.all_to_all_bytes = 2 * L.logical_route_bytes;
+  L.accepted_route_bytes = L.accepted_routes * hsz * be;
+  L.local_routes = h_cnt[LC_LOCAL_ALL];
+  L.cross_rank_routes = h_cnt[LC_CROSS_ALL];
+  L.cross_rank_dispatch_bytes = L.cross_rank_routes * hsz * be;
+  L.cross_rank_roundtrip_bytes = 2 * L.cross_rank_dispatch_bytes;
+  L.accepted_local_routes = h_cnt[LC_LOCAL_ACC];
+  L.accepted_cross_rank_routes = h_cnt[LC_CROSS_ACC];
+  L.accepted_cross_rank_dispatch_bytes = L.accepted_cross_rank_routes * hsz * be;
+  L.accepted_cross_rank_roundtrip_bytes = 2 * L.accepted_cross_rank_dispatch_bytes;
+  const double avg = (double)A / (double)E;
+  L.balance_ratio = avg > 0.0 ? (double)max_load / avg : 0.0;
+  const int64_t loc_total = L.local_routes + L.cross_rank_routes;
+  L.local_hit_ratio = loc_total ? (double)L.local_routes / (double)loc_total : 0.0;
+  const int64_t acc_total = L.accepted_local_routes + L.accepted_cross_rank_routes;
+  L.accepted_local_hit_ratio =
+      acc_total ? (double)L.accepted_local_routes / (double)acc_total : 0.0;
+  L.pair_bytes_uniform = (double)L.logical_route_bytes / (double)n_ep;
+  double sfp = 0.0;
+  for (int e = 0; e < E; ++e) {
+    const double fe = T ? (double)h_load[e] / (double)T : 0.0;
+    const double pe = T ? h_P[e] / (double)T : 0.0;
+    if (f) f[e] = fe;
+    if (P) P[e] = pe;
+    if (loads) loads[e] = h_load[e];
+    sfp += fe * pe;
+  }
+  if (T > 0) {
+    L.l_aux = alpha * sfp;
+    L.l_aux_norm = alpha * (double)E * sfp / (double)K;
+  }
+  const double mean = (double)sum_load / (double)E;
+  if (mean > 0.0 && E > 1) {
+    double ss = 0.0;
+    for (int e = 0; e < E; ++e) {
+      const double d = (double)h_load[e] - mean;
+      ss += d * d;
+    }
+    L.load_var_over_mean = (ss / (double)(E - 1)) / mean;
+  }
+  L.imbalanced = (mean > 0.0 && (double)max_load / mean > 2.0) ? 1 : 0;
+  if (pair_routes)
+    for (int j = 0; j < n_ep * n_ep; ++j) pair_routes[j] = h_pair[j];
+  L.status = MOE_OK;
+  if (h_cnt[LC_INVALID_ID] > 0) L.status = MOE_ERR_EXPERT_ID;
+  else if (h_cnt[LC_INVALID_RANK] > 0) L.status = MOE_ERR_INVALID_ARG;
+  *out = L;
+  return L.status;
+}
+
+}  // extern "C"

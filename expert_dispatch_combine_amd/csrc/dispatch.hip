@@ -1,0 +1,259 @@
+// Capacity-limited dispatch: expert histogram, per-expert offsets, each
+// route's rank within its expert, the capacity drop, and the gather of the
+// accepted token rows into contiguous per-expert segments.
+//
+// Method: "MoE大模型专家并行与动态路由优化" 3.3 (capacity loop: routes in
+// (token, k-slot) order, accept while the expert holds fewer than `capacity`)
+// with capacity = ceil((A/E) * capacity_factor) from "47. MoE Expert Parallel"
+// Step 3; dispatch = moving each accepted token to its expert
+// ("专家并行（Expert Parallelism）", Dispatch).
+//
+// The sequential loop is a stable counting sort by expert: a route's rank is
+// the number of earlier routes (row-major over [T, K]) with the same expert.
+//   count kernel  : LDS histogram of each 1024-route block  -> counts[b][E+1]
+//   slot kernel   : prefix over earlier blocks + in-block wave multisplit
+//                   (ballots on the id bits) -> rank, row, row_token, offsets
+//   gather kernel : x_disp[row] = x[row_token[row]] with 16-byte vectors
+#include "moe_internal.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int RPB = kDispatchRoutesPerBlock;  // routes per block
+constexpr int CHUNK = 256;                    // routes per pass (one per thread)
+
+__global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ idx,
+                                                    int64_t A, int E,
+                                                    int32_t* __restrict__ counts) {
+  __shared__ int hist[kMaxExperts + 1];
+  const int tid = threadIdx.x;
+  for (int e = tid; e <= E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * RPB;
+#pragma unroll
+  for (int j = 0; j < RPB / 256; ++j) {
+    const int64_t i = base + j * 256 + tid;
+    if (i < A) {
+      const int id = idx[i];
+      const int bin = (id >= 0 && id < E) ? id : E;  // bin E: invalid ids
+      atomicAdd(&hist[bin], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* out = counts + (size_t)blockIdx.x * (E + 1);
+  for (int e = tid; e <= E; e += 256) out[e] = hist[e];
+}
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sh_wave, int tid) {
+  // 256 threads = 4 waves
+  const int lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) sh_wave[wave] = incl;
+  __syncthreads();
+  int prefix = 0;
+  for (int w = 0; w < wave; ++w) prefix += sh_wave[w];
+  __syncthreads();
+  return prefix + incl - v;
+}
+
+__global__ __launch_bounds__(256) void slot_kernel(
+    const int32_t* __restrict__ idx, int64_t A, int K, int E, int64_t cap, int nblocks,
+    const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ route_rank, int32_t* __restrict__ route_row,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ load_out) {
+  __shared__ int run[kMaxExperts];       // next rank per expert for this block
+  __shared__ int off[kMaxExperts + 1];   // exclusive prefix of accepted counts
+  __shared__ int wcnt[4][kMaxExperts];   // per-wave counts of the current pass
+  __shared__ int ptot[kMaxExperts];     // partial column sums (S slices)
+  __shared__ int pbef[kMaxExperts];
+  __shared__ int sh_wave[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+
+  // 1. per expert: routes in earlier blocks (-> run) and in all blocks (load)
+  //    -> accepted = min(load, cap) -> exclusive scan over experts (-> off).
+  //    S threads share one expert's column of the count matrix.
+  const int S = (E >= 256) ? 1 : (256 / E);
+  for (int w = tid; w < E * S; w += 256) {
+    const int e = w % E, sl = w / E;
+    int bef = 0, tot = 0;
+#pragma unroll 4
+    for (int bb = sl; bb < nblocks; bb += S) {
+      const int c = counts[(size_t)bb * (E + 1) + e];
+      tot += c;
+      bef += (bb < b) ? c : 0;
+    }
+    ptot[w] = tot;
+    pbef[w] = bef;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    int bef = 0, tot = 0;
+    for (int sl = 0; sl < S; ++sl) {
+      tot += ptot[sl * E + e];
+      bef += pbef[sl * E + e];
+    }
+    run[e] = bef;
+    off[e] = (int)min((int64_t)tot, cap);  // accepted count, scanned in place below
+    if (b == 0 && load_out) load_out[e] = tot;
+  }
+  __syncthreads();
+  const int per_thread = (E + 255) / 256;  // consecutive experts per thread (<= 4)
+  int accv[4];
+  int my_acc = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid * per_thread + j;
+    accv[j] = (j < per_thread && e < E) ? off[e] : 0;
+    my_acc += accv[j];
+  }
+  int excl = block_exclusive_scan(my_acc, sh_wave, tid);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid * per_thread + j;
+    if (j < per_thread && e < E) {
+      off[e] = excl;
+      excl += accv[j];
+    }
+  }
+  if (tid == 255) off[E] = excl;  // the last thread ends at the grand total
+  __syncthreads();
+  if (b == 0)
+    for (int e = tid; e <= E; e += 256) offsets[e] = off[e];
+
+  // 2. ranks of this block's routes, 256 at a time
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t base = (int64_t)b * RPB;
+  for (int p = 0; p < RPB / CHUNK; ++p) {
+    const int64_t i = base + p * CHUNK + tid;
+    int id = -1;
+    if (i < A) id = idx[i];
+    const bool valid = (i < A) && id >= 0 && id < E;
+    for (int e = tid; e < 4 * E; e += 256) (&wcnt[0][0])[e / E * kMaxExperts + e % E] = 0;
+    __syncthreads();
+    // lanes of this wave holding the same expert id
+    uint64_t m = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = valid && ((id >> bit) & 1);
+      const uint64_t bm = __ballot(on);
+      m &= on ? bm : ~bm;
+    }
+    const int below = __popcll(m & lt_mask);
+    if (valid && below == 0) wcnt[wave][id] = __popcll(m);
+    __syncthreads();
+    int rank = -1;
+    if (valid) {
+      int prefix = run[id];
+      for (int w = 0; w < wave; ++w) prefix += wcnt[w][id];
+      rank = prefix + below;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) run[e] += wcnt[0][e] + wcnt[1][e] + wcnt[2][e] + wcnt[3][e];
+    if (i < A) {
+      route_rank[i] = rank;
+      int row = -1;
+      if (valid && (int64_t)rank < cap) {
+        row = off[id] + rank;
+        row_token[row] = (int)(i / K);
+      }
+      route_row[i] = row;
+    }
+    __syncthreads();
+  }
+}
+
+// x_disp[row] = x[row_token[row]] for row < R = offsets[E]; rows are
+// row_vecs 16-byte vectors long.  Each workgroup moves ROWS rows.
+template <int ROWS>
+__global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x,
+                                                     const int32_t* __restrict__ row_token,
+                                                     const int32_t* __restrict__ offsets,
+                                                     int E, int row_vecs,
+                                                     uint4* __restrict__ xd) {
+  const int R = offsets[E];
+  const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+  if (r0 >= R) return;
+  const int nrows = (int)min((int64_t)ROWS, (int64_t)R - r0);
+  const int total = nrows * row_vecs;
+  constexpr int U = 4;
+  for (int v0 = threadIdx.x; v0 < total; v0 += 256 * U) {
+    uint4 tmp[U];
+    int64_t dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u * 256;
+      dst[u] = -1;
+      if (v < total) {
+        const int r = v / row_vecs, c = v % row_vecs;
+        const int t = row_token[r0 + r];
+        tmp[u] = x[(int64_t)t * row_vecs + c];
+        dst[u] = (r0 + r) * row_vecs + c;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (dst[u] >= 0) xd[dst[u]] = tmp[u];
+  }
+}
+
+// the same gather for rows that are not a whole number of 16-byte vectors
+__global__ __launch_bounds__(256) void gather_bytes_kernel(const uint8_t* __restrict__ x,
+                                                           const int32_t* __restrict__ row_token,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int E, int64_t row_bytes,
+                                                           uint8_t* __restrict__ xd) {
+  const int R = offsets[E];
+  const int64_t row = blockIdx.x;
+  if (row >= R) return;
+  const int t = row_token[row];
+  for (int64_t c = threadIdx.x; c < row_bytes; c += 256)
+    xd[row * row_bytes + c] = x[(int64_t)t * row_bytes + c];
+}
+
+}  // namespace
+
+size_t dispatch_ws_bytes(int64_t A, int E) {
+  const int64_t nb = (A + RPB - 1) / RPB;
+  return align_up((size_t)(nb > 0 ? nb : 1) * (size_t)(E + 1) * sizeof(int32_t), 256);
+}
+
+hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int64_t A, int K, int E,
+                           int64_t cap, int64_t row_bytes, int64_t r_max,
+                           int32_t* offsets, int32_t* route_rank, int32_t* route_row,
+                           int32_t* row_token, void* x_disp, int32_t* load, void* ws,
+                           hipStream_t s) {
+  const int nb = (int)((A + RPB - 1) / RPB);
+  int32_t* counts = (int32_t*)ws;
+  if (nb > 0) {
+    hipLaunchKernelGGL(count_kernel, dim3(nb), dim3(256), 0, s, topk_idx, A, E, counts);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  // at least one block so that the offsets (all zero) are written
+  hipLaunchKernelGGL(slot_kernel, dim3(nb > 0 ? nb : 1), dim3(256), 0, s, topk_idx, A, K, E,
+                     cap, nb, counts, offsets, route_rank, route_row, row_token, load);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || r_max == 0) return err;
+  if (row_bytes % 16 == 0) {
+    constexpr int ROWS = 8;
+    const int64_t grid = (r_max + ROWS - 1) / ROWS;
+    hipLaunchKernelGGL((gather_kernel<ROWS>), dim3((unsigned)grid), dim3(256), 0, s,
+                       (const uint4*)x, row_token, offsets, E, (int)(row_bytes / 16),
+                       (uint4*)x_disp);
+  } else {
+    hipLaunchKernelGGL(gather_bytes_kernel, dim3((unsigned)r_max), dim3(256), 0, s,
+                       (const uint8_t*)x, row_token, offsets, E, row_bytes,
+                       (uint8_t*)x_disp);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

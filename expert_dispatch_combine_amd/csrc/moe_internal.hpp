@@ -1,0 +1,98 @@
+// Internal declarations shared by the HIP translation units of libmoe.
+// Device helpers (bf16 conversion, MFMA operand types) and the launchers each
+// kernel file exports to the C-ABI layer in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Limits of the kernels (validated on the host before any launch).
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxRanks = 64;
+
+// Routes handled by one workgroup of the dispatch count / slot kernels.
+constexpr int kDispatchRoutesPerBlock = 1024;
+// Routes handled by one workgroup of the ledger partial kernel.
+constexpr int kLedgerRoutesPerBlock = 2048;
+// Scalar counters of the ledger, per block and in the final area.
+enum LedgerCounter {
+  LC_LOCAL_ALL = 0,
+  LC_CROSS_ALL,
+  LC_LOCAL_ACC,
+  LC_CROSS_ACC,
+  LC_ACCEPTED,
+  LC_INVALID_ID,
+  LC_INVALID_RANK,
+  LC_COUNT_PAD,
+  LC_N = 8
+};
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) {
+  return __uint_as_float(v << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- workspace
+// Byte sizes of the per-call workspace regions (a call uses its own regions
+// from offset 0; regions of different calls may overlap).
+size_t dispatch_ws_bytes(int64_t A, int E);
+size_t ledger_ws_bytes(int64_t A, int E, int n_ep);
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the first HIP error.
+hipError_t launch_router_gemm_bf16(const uint16_t* x, const uint16_t* wg, float* logits,
+                                   int T, int h, int E, hipStream_t s);
+hipError_t launch_router_topk_bf16(const uint16_t* x, const uint16_t* wg, const float* bias,
+                                   float* logits, int32_t* idx, float* gate, int32_t* load,
+                                   int T, int h, int E, int K, hipStream_t s);
+hipError_t launch_router_gemm_f32(const float* x, const float* wg, float* logits, int T,
+                                  int h, int E, hipStream_t s);
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+hipError_t launch_topk_softmax(const float* logits, const float* bias, int32_t* idx,
+                               float* gate, int32_t* load, int T, int E, int K,
+                               hipStream_t s);
+
+hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int64_t A, int K, int E,
+                           int64_t cap, int64_t row_bytes, int64_t r_max,
+                           int32_t* offsets, int32_t* route_rank, int32_t* route_row,
+                           int32_t* row_token, void* x_disp, int32_t* load, void* ws,
+                           hipStream_t s);
+
+hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* offsets, const uint16_t* w1,
+                           const float* b1, const uint16_t* w2, const float* b2,
+                           uint16_t* hbuf, float* y, int E, int h, int F, int64_t r_max,
+                           hipStream_t s);
+hipError_t launch_ffn_f32(const float* xd, const int32_t* offsets, const float* w1,
+                          const float* b1, const float* w2, const float* b2, float* hbuf,
+                          float* y, int E, int h, int F, int64_t r_max, hipStream_t s);
+
+hipError_t launch_combine(const float* y, const int32_t* route_row, const float* gate,
+                          float* out, int T, int K, int h, hipStream_t s);
+
+// Ledger: per-block partials then a fixed-order reduction into `final_area`
+// (layout: loads[E] int64 | P[E] double | counters[LC_N] int64 |
+//  pairs[n_ep*n_ep] int64).
+hipError_t launch_ledger(const int32_t* idx, const float* gate, const int32_t* route_row,
+                         const int32_t* src, const int32_t* owner, int T, int K, int E,
+                         int n_ep, void* ws, void** final_area, size_t* final_bytes,
+                         hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,197 @@
+/*
+ * moe.h -- C ABI of a single-GPU (MI355X, gfx950) Mixture-of-Experts layer:
+ *          route -> capacity-limited dispatch -> expert FFN -> weighted combine,
+ *          plus a counters-only ledger.
+ *
+ * Pages cited (by title):
+ *   [EP47] "47. MoE Expert Parallel | MoE 专家并行" (llm-algo-leetcode, ch. 47)
+ *   [EP46] "46. MoE Expert Parallel | MoE 专家并行" (llm-algo-leetcode, ch. 46)
+ *   [EPC]  "专家并行（Expert Parallelism）" (tier6-model)
+ *   [DSV3] "MoE大模型专家并行与动态路由优化——从DeepSeek-V3到生产级推理架构"
+ *
+ * Conventions for every entry point
+ *   - All tensors are dense, row-major, on the device, allocated and owned by
+ *     the caller.  The library never allocates device memory and keeps no
+ *     state between calls; it is safe to call from several host threads on
+ *     different streams with different workspaces.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every entry point
+ *     except moe_ledger only enqueues work and returns; moe_ledger waits for
+ *     the stream (it copies the counters back to the host).
+ *   - Floating-point activations and weights are MOE_BF16 (bfloat16) or
+ *     MOE_F32 as cfg->dtype says; logits, gates, biases, expert outputs and
+ *     the layer output are always fp32.
+ *   - bf16 tensors and the dispatched buffer must be 16-byte aligned; on the
+ *     bf16 path h and F must be multiples of 64 (else MOE_ERR_UNSUPPORTED).
+ *   - Host-detectable errors (NULL pointers, sizes, K > E, capacity < 0,
+ *     workspace too small, owner rank >= n_ep) return before anything is
+ *     enqueued.  An expert id outside [0, E) inside a caller-built topk_idx is
+ *     detected on the device: dispatch drops such a route and moe_ledger
+ *     reports MOE_ERR_EXPERT_ID.  No exception crosses the ABI.
+ *   - Sizes: T tokens, h hidden size, E experts, K experts per token, F FFN
+ *     width, A = T*K routes, cap = capacity, R_max = min(A, E*cap) rows.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* NULL pointer, negative size, K > E, cf <= 0 ... */
+  MOE_ERR_EXPERT_ID = 2,    /* device-detected expert id outside [0, E)       */
+  MOE_ERR_SHAPE = 3,        /* inconsistent sizes (e.g. workspace too small)  */
+  MOE_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed      */
+  MOE_ERR_UNSUPPORTED = 5   /* valid, but outside what the kernels implement  */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Shape of one MoE layer invocation.  T may be 0 (an empty batch is valid
+ * and yields a zero ledger, [EP46] empty-route contract). */
+typedef struct moe_cfg {
+  int32_t T;        /* tokens                                     */
+  int32_t h;        /* hidden size (model dim)                    */
+  int32_t E;        /* experts, 1..1024                           */
+  int32_t K;        /* experts per token, 1..min(E, 32)           */
+  int32_t F;        /* expert FFN width                           */
+  int32_t dtype;    /* moe_dtype of x, W_g, W1, W2 and H          */
+  double capacity_factor;  /* > 0                                  */
+} moe_cfg;
+
+/* Counters of one routed batch ([EP47] route ledger, [EP46] ledger and
+ * dispatch-locality summaries, [DSV3] 3.2 load-balance terms).  Byte counts
+ * use bytes_per_elem = 4 (MOE_F32) or 2 (MOE_BF16). */
+typedef struct moe_ledger_t {
+  int64_t total_tokens;          /* T                                         */
+  int64_t total_routes;          /* A = T*K                                   */
+  int64_t num_experts;           /* E                                         */
+  int64_t capacity;              /* the capacity passed in                    */
+  int64_t accepted_routes;       /* R = routes with route_row >= 0            */
+  int64_t overflow;              /* sum_e max(load_e - capacity, 0)           */
+  int64_t max_load;              /* max_e load_e                              */
+  int64_t invalid_routes;        /* ids outside [0, E) (then status != OK)    */
+  int64_t logical_route_bytes;   /* A*h*bytes (= the pages' dispatch_bytes)   */
+  int64_t all_to_all_bytes;      /* 2 * logical_route_bytes                   */
+  int64_t accepted_route_bytes;  /* R*h*bytes                                 */
+  int64_t local_routes;          /* all routes with src_rank == owner_rank    */
+  int64_t cross_rank_routes;     /* all routes with src_rank != owner_rank    */
+  int64_t cross_rank_dispatch_bytes;   /* cross_rank_routes*h*bytes           */
+  int64_t cross_rank_roundtrip_bytes;  /* 2 * cross_rank_dispatch_bytes       */
+  int64_t accepted_local_routes;       /* same split over accepted routes     */
+  int64_t accepted_cross_rank_routes;
+  int64_t accepted_cross_rank_dispatch_bytes;
+  int64_t accepted_cross_rank_roundtrip_bytes;
+  int64_t n_ep;                  /* logical expert-parallel ranks             */
+  double balance_ratio;          /* max load / (A/E), 0.0 when A == 0         */
+  double local_hit_ratio;        /* local_routes / A, 0.0 when A == 0         */
+  double accepted_local_hit_ratio;
+  double pair_bytes_uniform;     /* logical_route_bytes / n_ep ([EPC])        */
+  double l_aux;                  /* alpha * sum_i f_i P_i                     */
+  double l_aux_norm;             /* alpha * E/K * sum_i f_i P_i               */
+  double alpha;
+  double load_var_over_mean;     /* unbiased variance of loads / mean load    */
+  int32_t imbalanced;            /* 1 when max/mean load > 2                  */
+  int32_t status;                /* MOE_OK or MOE_ERR_EXPERT_ID               */
+} moe_ledger_t;
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(int status);
+
+/* ceil((A / E) * capacity_factor) evaluated in IEEE double; 0 when A == 0;
+ * -1 for E <= 0, A < 0 or capacity_factor not > 0.
+ * [EP47] Step 3 (capacity), [EP46] TODO 1.  Pure host function. */
+int64_t moe_capacity(int64_t A, int32_t E, double capacity_factor);
+
+/* R_max = min(T*K, E*capacity): rows of the dispatched buffers. */
+int64_t moe_max_rows(const moe_cfg* cfg, int64_t capacity);
+
+/* Bytes of device workspace every call below needs for `cfg` (any n_ep up
+ * to 64).  The same workspace may be reused by successive calls on one
+ * stream; its contents need no initialisation. */
+size_t moe_workspace_bytes(const moe_cfg* cfg);
+
+/* Router: logits = x W_g^T (+ logit_bias), then per token the K largest
+ * logits (descending; equal logits -> lower expert id) and the softmax over
+ * those K ([DSV3] section 一 g = Softmax(TopK(W_g x)); 3.1 TopKGate).
+ *   x          [T, h]  dtype      token activations, or NULL: then `logits`
+ *                                 is an INPUT and the product is skipped
+ *   w_gate     [E, h]  dtype      router weight (ignored when x == NULL)
+ *   logit_bias [E]     fp32|NULL  added to every token's logits before the
+ *                                 top-k; the softmax uses the biased logits
+ *   logits     [T, E]  fp32       written (x != NULL) or read (x == NULL);
+ *                                 always WITHOUT the bias
+ *   topk_idx   [T, K]  int32      expert ids, slot 0 = largest
+ *   topk_gate  [T, K]  fp32       softmax weights, each row sums to 1
+ *   expert_load [E]    int32|NULL pre-capacity histogram of topk_idx
+ * The workspace is not used today (may be NULL). */
+int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate,
+              const float* logit_bias, float* logits, int32_t* topk_idx,
+              float* topk_gate, int32_t* expert_load, void* ws, size_t ws_bytes,
+              void* stream);
+
+/* Capacity-limited dispatch ([DSV3] 3.3 capacity loop; [EPC] Dispatch).
+ * Routes are taken in (token, k-slot) order; the first `capacity` routes of
+ * each expert are accepted and the rest dropped.  Accepted routes are packed
+ * per expert (experts in id order, tokens in order inside an expert):
+ *   expert_offsets [E+1] int32   exclusive prefix of min(load_e, capacity)
+ *   route_rank     [T,K] int32   routes to the same expert before this one
+ *                                (-1 for an invalid id)
+ *   route_row      [T,K] int32   offset[e] + rank if rank < capacity, else -1
+ *   row_token      [R_max] int32 token of each accepted row (rows >= R are
+ *                                left untouched)
+ *   x_disp         [R_max, h] dtype  x_disp[row] = x[row_token[row]]
+ *   expert_load    [E] int32|NULL    pre-capacity load of each expert
+ * ws: at least moe_workspace_bytes(cfg) bytes. */
+int moe_dispatch(const moe_cfg* cfg, const void* x, const int32_t* topk_idx,
+                 int64_t capacity, int32_t* expert_offsets, int32_t* route_rank,
+                 int32_t* route_row, int32_t* row_token, void* x_disp,
+                 int32_t* expert_load, void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFN over ragged expert segments ([DSV3] section 一
+ * FFN(x) = W2 GELU(W1 x + b1) + b2, GELU in its tanh form):
+ * for each expert e and row r in [offset[e], offset[e+1]):
+ *   H[r] = GELU_tanh(W1[e] x_disp[r] + b1[e])   stored as dtype (bf16 RNE)
+ *   Y[r] = W2[e] H[r] + b2[e]                    fp32
+ *   x_disp [R_max, h] dtype;  w1 [E, F, h] dtype;  b1 [E, F] fp32
+ *   w2 [E, h, F] dtype;  b2 [E, h] fp32;  h_buf [R_max, F] dtype (scratch,
+ *   holds H afterwards);  y [R_max, h] fp32.  Rows >= R are not written.
+ * `capacity` bounds R_max (the same value given to moe_dispatch). */
+int moe_expert_ffn(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
+                   const int32_t* expert_offsets, const void* w1, const float* b1,
+                   const void* w2, const float* b2, void* h_buf, float* y,
+                   void* stream);
+
+/* Weighted combine in original token order, without atomics ([EP46]
+ * combine_expert_outputs; [EPC] Combine):
+ *   out[t] = sum over k = 0..K-1 with route_row[t,k] >= 0 of
+ *            topk_gate[t,k] * y[route_row[t,k]]       (fp32, k ascending)
+ * A token whose routes were all dropped gets zeros.  out [T, h] fp32. */
+int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* route_row,
+                const float* topk_gate, float* out, void* stream);
+
+/* Counters-only ledger ([EP47] summarize, [EP46] summarize + dispatch
+ * locality, [DSV3] 2.2 placement and 3.2 auxiliary-loss terms).
+ *   topk_idx [T,K] int32, topk_gate [T,K] fp32, route_row [T,K] int32 (from
+ *   moe_dispatch), src_rank [T] int32 (token's source rank), owner_rank [E]
+ *   int32 (expert's rank, e.g. e % n_ep), n_ep in 1..64, alpha (0.01 on the
+ *   page).  Host outputs (each may be NULL except `out`): loads [E] int64,
+ *   f [E] and P [E] double (f_i = load_i / T, P_i = sum_t g_{t,i} / T),
+ *   pair_routes [n_ep*n_ep] int64 (accepted routes from source rank i to
+ *   owner rank j, row-major).
+ * Synchronises `stream`.  Returns MOE_ERR_EXPERT_ID (with `out` filled) when
+ * topk_idx holds an id outside [0, E). */
+int moe_ledger(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_gate,
+               const int32_t* route_row, int64_t capacity, const int32_t* src_rank,
+               const int32_t* owner_rank, int32_t n_ep, double alpha,
+               moe_ledger_t* out, int64_t* loads, double* f, double* P,
+               int64_t* pair_routes, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -116,8 +116,10 @@ def make_inputs(cfg: Config, device="cpu", with_experts: bool = True) -> Inputs:
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     T, h, E, F = cfg.T, cfg.h, cfg.E, cfg.F
     s = cfg.seed
-    x = _normal((T, h), 1.0, seed_for(s, "x"), device).to(dt)
-    w_gate = _normal((E, h), 1.0 / math.sqrt(h), seed_for(s, "w_gate"), device).to(dt)
+    # router inputs are drawn on the CPU (device-independent values, so the
+    # routing can be reproduced anywhere); expert weights on `device`
+    x = _normal((T, h), 1.0, seed_for(s, "x"), "cpu").to(dt).to(device)
+    w_gate = _normal((E, h), 1.0 / math.sqrt(h), seed_for(s, "w_gate"), "cpu").to(dt).to(device)
     if with_experts:
         w1 = torch.empty((E, F, h), dtype=dt, device=device)
         w2 = torch.empty((E, h, F), dtype=dt, device=device)

@@ -1,0 +1,201 @@
+"""moe_expert_ffn and moe_combine on the GPU vs the oracle, each fed the
+oracle's own inputs (its dispatched rows, its expert outputs), so each kernel
+is checked on its own.
+
+Tolerances (derived, written out in each test):
+  H (bf16): the oracle rounds the exact f64 value, the GPU an fp32-accumulated
+     one; both land on the bf16 grid, so they differ by at most one bf16 ulp
+     (<= 2^-7 |H|) plus the pre-activation error (<= h u sum|x W1|, GELU'
+     <= 1.13).
+  Y (fp32): |dY_n| <= sum_f |dH_f| |W2_nf| + F u sum_f |H_f W2_nf| + u |Y|;
+     and in RMS, dY must stay below 2^-8 RMS(Y), far under what any indexing
+     or operand mistake produces.
+  out: fp32 fma of K terms: |d| <= (K+1) u sum_k |g_k Y_k|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import expert_dispatch_combine_amd as M
+import moe_workloads as W
+import oracle as O
+from expert_dispatch_combine_amd.runner import LayerBuffers
+from gpu_util import (U32, banner, bias_np, custom_inputs, device_inputs, host, rms, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_dispatch(inp: W.Inputs):
+    cfg = inp.cfg
+    x64 = host(inp.x)
+    logits = O.router_logits(x64, host(inp.w_gate))
+    idx, gate = O.topk_softmax(logits, cfg.K, bias_np(inp))
+    cap = O.capacity(cfg.T * cfg.K, cfg.E, cfg.cf)
+    sl = O.slot_routes(idx, cfg.E, cap)
+    return idx, gate, cap, sl
+
+
+def _run_ffn(inp: W.Inputs, cap, sl):
+    cfg = inp.cfg
+    mc = M.MoeCfg.make(cfg.T, cfg.h, cfg.E, cfg.K, cfg.F, cfg.dtype, cfg.cf)
+    b = LayerBuffers(mc, cap)
+    R = sl["R"]
+    if R:
+        b.x_disp[:R].copy_(inp.x[torch.from_numpy(sl["row_token"].astype(np.int64)).cuda()])
+    b.expert_offsets.copy_(torch.from_numpy(sl["expert_offsets"]))
+    M.moe_expert_ffn(mc, cap, b.x_disp, b.expert_offsets, inp.w1, inp.b1, inp.w2, inp.b2,
+                     b.h_buf, b.y)
+    torch.cuda.synchronize()
+    return b
+
+
+def _check_rows(inp, sl, b, rows):
+    """Compare H and Y of the given dispatched rows with the oracle's."""
+    cfg = inp.cfg
+    if len(rows) == 0:
+        return
+    offs = sl["expert_offsets"]
+    experts = np.searchsorted(offs, rows, side="right") - 1
+    x64 = host(inp.x)[sl["row_token"][rows]]
+    h_round = "bf16" if cfg.dtype == "bf16" else "f32"
+    Hg = b.h_buf[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    Yg = b.y[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    for e in np.unique(experts):
+        m = experts == e
+        w1 = host(inp.w1[int(e)])
+        w2 = host(inp.w2[int(e)])
+        b1 = host(inp.b1[int(e)])
+        b2 = host(inp.b2[int(e)])
+        xe = x64[m]
+        u = xe @ w1.T + b1
+        H = O.gelu_tanh(u)
+        H = O.round_bf16(H) if h_round == "bf16" else O.round_f32(H)
+        Y = O.round_f32(H @ w2.T + b2)
+        du = cfg.h * U32 * (np.abs(xe) @ np.abs(w1).T) + U32 * np.abs(u)
+        ulp = 2.0 ** -7 if h_round == "bf16" else 2.0 ** -23
+        tolH = ulp * np.abs(H) + 1.13 * du + 1e-6
+        dH = np.abs(Hg[m] - H)
+        assert np.all(dH <= tolH), float((dH - tolH).max())
+        if h_round == "bf16":
+            assert np.mean(dH > 0) < 0.02
+        tolY = (ulp * np.abs(H) + 1.13 * du) @ np.abs(w2).T \
+            + cfg.F * U32 * (np.abs(H) @ np.abs(w2).T) + U32 * np.abs(Y) + 1e-6
+        dY = np.abs(Yg[m] - Y)
+        assert np.all(dY <= tolY), float((dY - tolY).max())
+        assert rms(Yg[m] - Y) <= 2.0 ** -8 * rms(Y) + 1e-7
+
+
+@pytest.mark.parametrize("cid", [1, 2, 5])
+def test_ffn_full_on_workloads(cid):
+    banner(f"ffn full config {cid}")
+    inp = device_inputs(cid)
+    _, _, cap, sl = _oracle_dispatch(inp)
+    b = _run_ffn(inp, cap, sl)
+    _check_rows(inp, sl, b, np.arange(sl["R"]))
+
+
+@pytest.mark.parametrize("cid", [3, 4])
+def test_ffn_sampled_rows_full_size(cid):
+    """Full-size workloads, launched exactly as the layer launches them;
+    a sample of rows (every expert's first and last row, plus random rows)
+    is checked against the oracle row by row."""
+    banner(f"ffn sampled config {cid}")
+    inp = device_inputs(cid)
+    _, _, cap, sl = _oracle_dispatch(inp)
+    b = _run_ffn(inp, cap, sl)
+    offs = sl["expert_offsets"]
+    rng = np.random.default_rng(cid)
+    rows = set()
+    for e in range(inp.cfg.E):
+        if offs[e + 1] > offs[e]:
+            rows.update({int(offs[e]), int(offs[e + 1] - 1)})
+    rows.update(rng.integers(0, sl["R"], 48).tolist())
+    rows = np.array(sorted(rows))
+    if cid == 4:  # 256 experts: keep the per-expert weight copies bounded
+        rows = rows[rng.permutation(len(rows))[:96]]
+        rows.sort()
+    _check_rows(inp, sl, b, rows)
+
+
+@pytest.mark.parametrize("T,h,E,K,F,cf", [(1, 64, 1, 1, 64, 1.0), (300, 128, 5, 2, 192, 0.8),
+                                          (1000, 256, 16, 2, 320, 1.0),
+                                          (513, 64, 64, 6, 128, 1.0),
+                                          (2500, 192, 3, 1, 448, 1.5)])
+def test_ffn_ragged_segments(T, h, E, K, F, cf):
+    banner(f"ffn ragged T={T} h={h} E={E} K={K} F={F}")
+    cfg = W.custom(T=T, h=h, E=E, K=K, F=F, cf=cf, dtype="bf16", seed=T * 7 + F)
+    inp = custom_inputs(cfg)
+    _, _, cap, sl = _oracle_dispatch(inp)
+    b = _run_ffn(inp, cap, sl)
+    _check_rows(inp, sl, b, np.arange(sl["R"]))
+
+
+def test_ffn_fp32_odd_sizes():
+    banner("ffn fp32 odd sizes")
+    cfg = W.custom(T=50, h=7, E=3, K=2, F=5, cf=1.0, dtype="f32", seed=4)
+    inp = custom_inputs(cfg)
+    _, _, cap, sl = _oracle_dispatch(inp)
+    b = _run_ffn(inp, cap, sl)
+    _check_rows(inp, sl, b, np.arange(sl["R"]))
+
+
+# ------------------------------------------------------------------ combine
+def _check_combine(T, K, h, R, drop_frac, seed):
+    rng = np.random.default_rng(seed)
+    Y = rng.standard_normal((max(R, 1), h)).astype(np.float32)
+    gate = rng.random((T, K)).astype(np.float32)
+    rows = np.full((T, K), -1, np.int32)
+    perm = rng.permutation(R)
+    flat = rows.reshape(-1)
+    take = min(R, T * K)
+    pos = rng.permutation(T * K)[:take]
+    flat[pos] = perm[:take]
+    flat[rng.random(T * K) < drop_frac] = -1
+    if T:
+        rows[0, :] = -1
+    mc = M.MoeCfg.make(T, h, max(K, 4), K, 64, "f32", 1.0)
+    out = torch.full((T, h), 7.0, device="cuda")
+    M.moe_combine(mc, to_dev(Y, torch.float32), to_dev(rows, torch.int32),
+                  to_dev(gate, torch.float32), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    want = O.combine(Y, rows, gate)
+    mag = np.zeros((T, h))
+    for k in range(K):
+        m = rows[:, k] >= 0
+        mag[m] += np.abs(gate[m, k][:, None].astype(np.float64) * Y[rows[m, k]])
+    assert np.all(np.abs(got - want) <= (K + 1) * U32 * mag + 1e-30)
+    if T:
+        assert np.all(got[0] == 0.0)
+
+
+@pytest.mark.parametrize("T,K,h,R,drop", [(1, 1, 4, 1, 0.0), (64, 2, 32, 119, 0.1),
+                                          (2048, 1, 768, 2048, 0.0), (300, 8, 100, 2000, 0.3),
+                                          (1000, 6, 2048, 3000, 0.5), (77, 3, 13, 50, 0.2)])
+def test_combine(T, K, h, R, drop):
+    banner(f"combine T={T} K={K} h={h}")
+    _check_combine(T, K, h, R, drop, seed=T + h)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 4, 5])
+def test_combine_on_workload_routing(cid):
+    """Combine with the workload's own routing and oracle expert outputs."""
+    banner(f"combine config {cid}")
+    inp = device_inputs(cid, with_experts=cid in (3, 4))
+    idx, gate, cap, sl = _oracle_dispatch(inp)
+    cfg = inp.cfg
+    R = max(sl["R"], 1)
+    rng = np.random.default_rng(cid)
+    Y = rng.standard_normal((R, cfg.h)).astype(np.float32)  # stands in for expert outputs
+    mc = M.MoeCfg.make(cfg.T, cfg.h, cfg.E, cfg.K, cfg.F, cfg.dtype, cfg.cf)
+    out = torch.empty((cfg.T, cfg.h), device="cuda")
+    M.moe_combine(mc, to_dev(Y, torch.float32), to_dev(sl["route_row"], torch.int32),
+                  to_dev(gate, torch.float32), out)
+    torch.cuda.synchronize()
+    want = O.combine(Y, sl["route_row"], gate)
+    got = out.cpu().numpy()
+    mag = np.zeros_like(want)
+    for k in range(cfg.K):
+        m = sl["route_row"][:, k] >= 0
+        mag[m] += np.abs(gate[m, k][:, None].astype(np.float64) * Y[sl["route_row"][m, k]])
+    assert np.all(np.abs(got - want) <= (cfg.K + 1) * U32 * mag + 1e-30)

@@ -1,0 +1,124 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/moe.h
+declares, and its pure-host functions and argument checks behave (no GPU call
+is made here: every invalid argument is rejected before any HIP call)."""
+import ctypes
+import math
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import expert_dispatch_combine_amd as M
+import oracle as O
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(moe_[a-z_]+)\s*\(", src,
+                                 flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.library_path()):
+        pytest.fail("libmoe.so is not built: run `python -m expert_dispatch_combine_amd.build`")
+    return M.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert set(names) == set(M.EXPORTED_SYMBOLS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert M.moe_status_string(0) == "MOE_OK"
+    assert M.moe_status_string(2) == "MOE_ERR_EXPERT_ID"
+    assert M.moe_status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def test_capacity_matches_oracle_bit_for_bit(lib):
+    rng = random.Random(0)
+    cases = [(11, 2, 1.0), (0, 4, 1.25), (2048, 16, 1.25), (8192, 8, 1.25), (32768, 256, 1.0),
+             (98304, 64, 1.0), (128, 4, 1.0), (7, 3, 1.1), (1, 1024, 0.01)]
+    for _ in range(3000):
+        cases.append((rng.randrange(0, 1 << 22), rng.randrange(1, 1025),
+                      rng.choice([1.0, 1.25, 2.0, 0.5, rng.uniform(0.01, 4.0)])))
+    for A, E, cf in cases:
+        assert M.moe_capacity(A, E, cf) == O.capacity(A, E, cf), (A, E, cf)
+    assert M.moe_capacity(4, 0, 1.0) == -1
+    assert M.moe_capacity(4, 2, 0.0) == -1
+    assert M.moe_capacity(4, 2, float("nan")) == -1
+    assert M.moe_capacity(-1, 2, 1.0) == -1
+
+
+def test_max_rows_and_workspace(lib):
+    cfg = M.MoeCfg.make(4096, 7168, 256, 8, 2048, "bf16", 1.0)
+    assert M.moe_max_rows(cfg, 128) == min(4096 * 8, 256 * 128)
+    assert M.moe_max_rows(cfg, 1000) == 4096 * 8
+    assert M.moe_max_rows(cfg, -1) == -1
+    assert M.moe_workspace_bytes(cfg) > 0
+    bad = M.MoeCfg.make(4, 64, 2, 3, 64, "bf16", 1.0)   # K > E
+    assert M.moe_workspace_bytes(bad) == 0
+
+
+def _call_route(lib, cfg):
+    return lib.moe_route(ctypes.byref(cfg), None, None, None, None, None, None, None, None, 0,
+                         None)
+
+
+def test_invalid_arguments_are_rejected_on_the_host(lib):
+    mk = M.MoeCfg.make
+    assert _call_route(lib, mk(4, 64, 2, 3, 64, "bf16", 1.0)) == 1          # K > E
+    assert _call_route(lib, mk(4, 64, 0, 1, 64, "bf16", 1.0)) == 1          # E = 0
+    assert _call_route(lib, mk(4, 0, 2, 1, 64, "bf16", 1.0)) == 1           # h = 0
+    assert _call_route(lib, mk(-1, 64, 2, 1, 64, "bf16", 1.0)) == 1         # T < 0
+    assert _call_route(lib, mk(4, 64, 2, 1, 64, "bf16", 0.0)) == 1          # cf = 0
+    assert _call_route(lib, mk(4, 64, 2, 1, 64, "bf16", float("inf"))) == 1
+    assert _call_route(lib, M.MoeCfg(4, 64, 2, 1, 64, 7, 1.0)) == 1          # dtype
+    assert _call_route(lib, mk(4, 64, 2000, 1, 64, "bf16", 1.0)) == 5       # E > 1024
+    assert _call_route(lib, mk(4, 64, 64, 33, 64, "bf16", 1.0)) == 5        # K > 32
+    assert _call_route(lib, mk(4, 96, 2, 1, 64, "bf16", 1.0)) == 5          # h % 64
+    assert _call_route(lib, mk(4, 64, 2, 1, 64, "bf16", 1.0)) == 1          # NULL outputs
+    cfg = mk(4, 64, 2, 1, 64, "bf16", 1.0)
+    # dispatch: negative capacity, missing workspace
+    assert lib.moe_dispatch(ctypes.byref(cfg), None, None, -1, None, None, None, None, None,
+                            None, None, 0, None) == 1
+    assert lib.moe_dispatch(ctypes.byref(cfg), None, None, 2, None, None, None, None, None,
+                            None, None, 0, None) == 1
+    # ffn: negative capacity, NULL operands
+    assert lib.moe_expert_ffn(ctypes.byref(cfg), -1, None, None, None, None, None, None, None,
+                              None, None) == 1
+    assert lib.moe_expert_ffn(ctypes.byref(cfg), 2, None, None, None, None, None, None, None,
+                              None, None) == 1
+    # combine: NULL outputs
+    assert lib.moe_combine(ctypes.byref(cfg), None, None, None, None, None) == 1
+    # ledger: n_ep out of range, NULL out
+    out = M.MoeLedger()
+    assert lib.moe_ledger(ctypes.byref(cfg), None, None, None, 2, None, None, 65, 0.01,
+                          ctypes.byref(out), None, None, None, None, None, 0, None) == 1
+    assert lib.moe_ledger(ctypes.byref(cfg), None, None, None, 2, None, None, 2, 0.01,
+                          None, None, None, None, None, None, 0, None) == 1
+
+
+def test_empty_batch_needs_no_device_work(lib):
+    cfg = M.MoeCfg.make(0, 64, 4, 2, 64, "bf16", 1.0)
+    # T = 0 with no expert_load requested: nothing is enqueued
+    assert lib.moe_route(ctypes.byref(cfg), None, None, None, None, None, None, None, None, 0,
+                         None) == 0
+    assert lib.moe_expert_ffn(ctypes.byref(cfg), 0, None, None, None, None, None, None, None,
+                              None, None) == 0
+    assert lib.moe_combine(ctypes.byref(cfg), None, None, None, None, None) == 0
+
+
+def test_ledger_struct_layout_matches_header(lib):
+    # 20 int64 + 8 double + 2 int32
+    assert ctypes.sizeof(M.MoeLedger) == 20 * 8 + 8 * 8 + 2 * 4
+    assert ctypes.sizeof(M.MoeCfg) == 6 * 4 + 8
