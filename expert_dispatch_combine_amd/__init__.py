@@ -9,14 +9,17 @@ there is no fallback: if libmoe.so is missing or fails to load, every call
 raises.
 """
 from ._binding import (  # noqa: F401
-    MOE_BF16, MOE_F32, MoeCfg, MoeError, MoeLedger, library_path, load_library,
-    moe_capacity, moe_combine, moe_dispatch, moe_expert_ffn, moe_ledger, moe_max_rows,
-    moe_route, moe_status_string, moe_workspace_bytes, EXPORTED_SYMBOLS,
+    EXPORTED_SYMBOLS, MOE_BF16, MOE_F32, MoeCfg, MoeError, MoeLedger, library_path,
+    load_library, moe_capacity, moe_combine, moe_dispatch, moe_expert_ffn,
+    moe_expert_ffn_packed, moe_ledger, moe_ledger_finalize, moe_ledger_launch,
+    moe_ledger_stage_bytes, moe_max_rows, moe_pack_expert_weights, moe_route,
+    moe_status_string, moe_workspace_bytes,
 )
 
 __all__ = [
-    "MOE_BF16", "MOE_F32", "MoeCfg", "MoeError", "MoeLedger", "library_path", "load_library",
-    "moe_capacity", "moe_combine", "moe_dispatch", "moe_expert_ffn", "moe_ledger",
-    "moe_max_rows", "moe_route", "moe_status_string", "moe_workspace_bytes",
-    "EXPORTED_SYMBOLS",
+    "EXPORTED_SYMBOLS", "MOE_BF16", "MOE_F32", "MoeCfg", "MoeError", "MoeLedger",
+    "library_path", "load_library", "moe_capacity", "moe_combine", "moe_dispatch",
+    "moe_expert_ffn", "moe_expert_ffn_packed", "moe_ledger", "moe_ledger_finalize",
+    "moe_ledger_launch", "moe_ledger_stage_bytes", "moe_max_rows", "moe_pack_expert_weights",
+    "moe_route", "moe_status_string", "moe_workspace_bytes",
 ]

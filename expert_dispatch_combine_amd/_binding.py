@@ -22,6 +22,8 @@ _LIB_NAME = "libmoe.so"
 EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_capacity", "moe_max_rows", "moe_workspace_bytes",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_ledger",
+    "moe_ledger_stage_bytes", "moe_ledger_launch", "moe_ledger_finalize",
+    "moe_expert_ffn_packed", "moe_pack_expert_weights",
 )
 
 
@@ -101,6 +103,18 @@ def load_library():
     lib.moe_ledger.restype = ctypes.c_int
     lib.moe_ledger.argtypes = [cfgp, P, P, P, _I64, P, P, ctypes.c_int32, _F64,
                                ctypes.POINTER(MoeLedger), P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_ledger_stage_bytes.restype = ctypes.c_size_t
+    lib.moe_ledger_stage_bytes.argtypes = [cfgp, ctypes.c_int32]
+    lib.moe_ledger_launch.restype = ctypes.c_int
+    lib.moe_ledger_launch.argtypes = [cfgp, P, P, P, P, P, ctypes.c_int32, P, ctypes.c_size_t,
+                                      P, ctypes.c_size_t, P]
+    lib.moe_ledger_finalize.restype = ctypes.c_int
+    lib.moe_ledger_finalize.argtypes = [cfgp, _I64, ctypes.c_int32, _F64, P,
+                                        ctypes.POINTER(MoeLedger), P, P, P, P]
+    lib.moe_expert_ffn_packed.restype = ctypes.c_int
+    lib.moe_expert_ffn_packed.argtypes = [cfgp, _I64, P, P, P, P, P, P, P, P, P]
+    lib.moe_pack_expert_weights.restype = ctypes.c_int
+    lib.moe_pack_expert_weights.argtypes = [cfgp, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -208,6 +222,29 @@ def moe_expert_ffn(cfg: MoeCfg, capacity: int, x_disp, expert_offsets, w1, b1, w
     _check("moe_expert_ffn", st)
 
 
+def moe_expert_ffn_packed(cfg: MoeCfg, capacity: int, x_disp, expert_offsets, w1_packed, b1,
+                          w2_packed, b2, h_buf, y, stream=None) -> None:
+    lib = load_library()
+    st = lib.moe_expert_ffn_packed(ctypes.byref(cfg), int(capacity),
+                                   _ptr(x_disp, "act", cfg, "x_disp"),
+                                   _ptr(expert_offsets, "i32", cfg, "expert_offsets"),
+                                   _ptr(w1_packed, "act", cfg, "w1_packed"),
+                                   _ptr(b1, "f32", cfg, "b1"),
+                                   _ptr(w2_packed, "act", cfg, "w2_packed"),
+                                   _ptr(b2, "f32", cfg, "b2"), _ptr(h_buf, "act", cfg, "h_buf"),
+                                   _ptr(y, "f32", cfg, "y"), _stream(stream))
+    _check("moe_expert_ffn_packed", st)
+
+
+def moe_pack_expert_weights(cfg: MoeCfg, w1, w2, w1_packed, w2_packed, stream=None) -> None:
+    lib = load_library()
+    st = lib.moe_pack_expert_weights(ctypes.byref(cfg), _ptr(w1, "act", cfg, "w1"),
+                                     _ptr(w2, "act", cfg, "w2"),
+                                     _ptr(w1_packed, "act", cfg, "w1_packed"),
+                                     _ptr(w2_packed, "act", cfg, "w2_packed"), _stream(stream))
+    _check("moe_pack_expert_weights", st)
+
+
 def moe_combine(cfg: MoeCfg, y, route_row, topk_gate, out, stream=None) -> None:
     lib = load_library()
     st = lib.moe_combine(ctypes.byref(cfg), _ptr(y, "f32", cfg, "y"),
@@ -238,6 +275,56 @@ def moe_ledger(cfg: MoeCfg, topk_idx, topk_gate, route_row, capacity: int, src_r
                         ctypes.byref(out), loads, f, P, pair, wsp, wsb, _stream(stream))
     if st != 0 and (raise_on_error or st not in (2, 1)):
         raise MoeError("moe_ledger", st)
+    d = out.as_dict()
+    d["loads"] = list(loads)
+    d["f"] = list(f)
+    d["P"] = list(P)
+    d["pair_routes"] = [list(pair[i * n_ep:(i + 1) * n_ep]) for i in range(n_ep)]
+    d["return_status"] = st
+    return d
+
+
+def moe_ledger_stage_bytes(cfg: MoeCfg, n_ep: int) -> int:
+    return int(load_library().moe_ledger_stage_bytes(ctypes.byref(cfg), int(n_ep)))
+
+
+def _host_ptr(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cpu" or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous host tensor")
+    return ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size()
+
+
+def moe_ledger_launch(cfg: MoeCfg, topk_idx, topk_gate, route_row, src_rank, owner_rank,
+                      n_ep: int, host_stage: torch.Tensor, ws=None, stream=None) -> None:
+    """Enqueue the ledger's kernels and the copy of its counters into
+    `host_stage` (a page-locked host tensor of moe_ledger_stage_bytes bytes)."""
+    lib = load_library()
+    wsp, wsb = _ws(ws)
+    hp, hb = _host_ptr(host_stage, "host_stage")
+    st = lib.moe_ledger_launch(ctypes.byref(cfg), _ptr(topk_idx, "i32", cfg, "topk_idx"),
+                               _ptr(topk_gate, "f32", cfg, "topk_gate"),
+                               _ptr(route_row, "i32", cfg, "route_row"),
+                               _ptr(src_rank, "i32", cfg, "src_rank"),
+                               _ptr(owner_rank, "i32", cfg, "owner_rank"), int(n_ep), hp, hb,
+                               wsp, wsb, _stream(stream))
+    _check("moe_ledger_launch", st)
+
+
+def moe_ledger_finalize(cfg: MoeCfg, capacity: int, n_ep: int, alpha: float,
+                        host_stage: torch.Tensor, raise_on_error: bool = True) -> dict:
+    """Decode a completed stage into the ledger dict (pure host call)."""
+    lib = load_library()
+    hp, _ = _host_ptr(host_stage, "host_stage")
+    E = int(cfg.E)
+    out = MoeLedger()
+    loads = (_I64 * E)()
+    f = (_F64 * E)()
+    P = (_F64 * E)()
+    pair = (_I64 * (n_ep * n_ep))()
+    st = lib.moe_ledger_finalize(ctypes.byref(cfg), int(capacity), int(n_ep), float(alpha), hp,
+                                 ctypes.byref(out), loads, f, P, pair)
+    if st != 0 and (raise_on_error or st not in (2, 1)):
+        raise MoeError("moe_ledger_finalize", st)
     d = out.as_dict()
     d["loads"] = list(loads)
     d["f"] = list(f)

@@ -131,12 +131,14 @@ int moe_dispatch(const moe_cfg* cfg, const void* x, const int32_t* topk_idx, int
                                     expert_load, ws, (hipStream_t)stream));
 }
 
-int moe_expert_ffn(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
-                   const int32_t* expert_offsets, const void* w1, const float* b1,
-                   const void* w2, const float* b2, void* h_buf, float* y, void* stream) {
+static int expert_ffn_common(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
+                             const int32_t* expert_offsets, const void* w1, const float* b1,
+                             const void* w2, const float* b2, void* h_buf, float* y,
+                             bool packed, void* stream) {
   int st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (packed && cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   const int64_t rmax = rows_max(cfg, capacity);
   if (rmax == 0) return MOE_OK;
   if (!x_disp || !expert_offsets || !w1 || !b1 || !w2 || !b2 || !h_buf || !y)
@@ -148,11 +150,50 @@ int moe_expert_ffn(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
       return MOE_ERR_INVALID_ARG;
     return hip_status(launch_ffn_bf16((const uint16_t*)x_disp, expert_offsets,
                                       (const uint16_t*)w1, b1, (const uint16_t*)w2, b2,
-                                      (uint16_t*)h_buf, y, cfg->E, cfg->h, cfg->F, rmax, s));
+                                      (uint16_t*)h_buf, y, cfg->E, cfg->h, cfg->F,
+                                      routes_of(cfg), capacity, rmax, packed, s));
   }
   return hip_status(launch_ffn_f32((const float*)x_disp, expert_offsets, (const float*)w1, b1,
                                    (const float*)w2, b2, (float*)h_buf, y, cfg->E, cfg->h,
                                    cfg->F, rmax, s));
+}
+
+int moe_expert_ffn(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
+                   const int32_t* expert_offsets, const void* w1, const float* b1,
+                   const void* w2, const float* b2, void* h_buf, float* y, void* stream) {
+  return expert_ffn_common(cfg, capacity, x_disp, expert_offsets, w1, b1, w2, b2, h_buf, y,
+                           false, stream);
+}
+
+int moe_expert_ffn_packed(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
+                          const int32_t* expert_offsets, const void* w1_packed,
+                          const float* b1, const void* w2_packed, const float* b2,
+                          void* h_buf, float* y, void* stream) {
+  return expert_ffn_common(cfg, capacity, x_disp, expert_offsets, w1_packed, b1, w2_packed,
+                           b2, h_buf, y, true, stream);
+}
+
+int moe_pack_expert_weights(const moe_cfg* cfg, const void* w1, const void* w2,
+                            void* w1_packed, void* w2_packed, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((w1 == nullptr) != (w1_packed == nullptr) || (w2 == nullptr) != (w2_packed == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if ((w1 && (!aligned16(w1) || !aligned16(w1_packed))) ||
+      (w2 && (!aligned16(w2) || !aligned16(w2_packed))))
+    return MOE_ERR_INVALID_ARG;
+  if ((w1 && w1 == w1_packed) || (w2 && w2 == w2_packed)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (w1) {
+    st = hip_status(launch_pack_weights((const uint16_t*)w1, (uint16_t*)w1_packed, cfg->E,
+                                        cfg->F, cfg->h, s));
+    if (st != MOE_OK) return st;
+  }
+  if (w2)
+    st = hip_status(launch_pack_weights((const uint16_t*)w2, (uint16_t*)w2_packed, cfg->E,
+                                        cfg->h, cfg->F, s));
+  return st;
 }
 
 int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* route_row,
@@ -166,32 +207,47 @@ int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* route_row,
                                    (hipStream_t)stream));
 }
 
-int moe_ledger(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_gate,
-               const int32_t* route_row, int64_t capacity, const int32_t* src_rank,
-               const int32_t* owner_rank, int32_t n_ep, double alpha, moe_ledger_t* out,
-               int64_t* loads, double* f, double* P, int64_t* pair_routes, void* ws,
-               size_t ws_bytes, void* stream) {
+size_t moe_ledger_stage_bytes(const moe_cfg* cfg, int32_t n_ep) {
+  if (check_cfg(cfg) != MOE_OK || n_ep < 1 || n_ep > kMaxRanks) return 0;
+  return ledger_final_bytes(cfg->E, n_ep);
+}
+
+int moe_ledger_launch(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_gate,
+                      const int32_t* route_row, const int32_t* src_rank,
+                      const int32_t* owner_rank, int32_t n_ep, void* host_stage,
+                      size_t stage_bytes, void* ws, size_t ws_bytes, void* stream) {
   int st = check_cfg(cfg);
   if (st != MOE_OK) return st;
-  if (!out || !owner_rank || !ws || capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (!owner_rank || !ws || !host_stage) return MOE_ERR_INVALID_ARG;
   if (n_ep < 1 || n_ep > kMaxRanks) return MOE_ERR_INVALID_ARG;
   const int T = cfg->T, K = cfg->K, E = cfg->E;
   if (T > 0 && (!topk_idx || !topk_gate || !route_row || !src_rank)) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < moe_workspace_bytes(cfg)) return MOE_ERR_SHAPE;
+  if (stage_bytes < ledger_final_bytes(E, n_ep)) return MOE_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   void* fin = nullptr;
   size_t fin_bytes = 0;
   st = hip_status(launch_ledger(topk_idx, topk_gate, route_row, src_rank, owner_rank, T, K, E,
                                 n_ep, ws, &fin, &fin_bytes, s));
   if (st != MOE_OK) return st;
-  std::vector<char> host(fin_bytes);
-  if (hipMemcpyAsync(host.data(), fin, fin_bytes, hipMemcpyDeviceToHost, s) != hipSuccess)
+  if (hipMemcpyAsync(host_stage, fin, fin_bytes, hipMemcpyDeviceToHost, s) != hipSuccess)
     return MOE_ERR_HIP;
-  if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
-  const int64_t* h_load = (const int64_t*)host.data();
-  const double* h_P = (const double*)(host.data() + (size_t)E * 8);
-  const int64_t* h_cnt = (const int64_t*)(host.data() + (size_t)2 * E * 8);
-  const int64_t* h_pair = (const int64_t*)(host.data() + (size_t)(2 * E + LC_N) * 8);
+  return MOE_OK;
+}
+
+int moe_ledger_finalize(const moe_cfg* cfg, int64_t capacity, int32_t n_ep, double alpha,
+                        const void* host_stage, moe_ledger_t* out, int64_t* loads, double* f,
+                        double* P, int64_t* pair_routes) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!out || !host_stage || capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (n_ep < 1 || n_ep > kMaxRanks) return MOE_ERR_INVALID_ARG;
+  const int T = cfg->T, K = cfg->K, E = cfg->E;
+  const char* stage = (const char*)host_stage;
+  const int64_t* h_load = (const int64_t*)stage;
+  const double* h_P = (const double*)(stage + (size_t)E * 8);
+  const int64_t* h_cnt = (const int64_t*)(stage + (size_t)2 * E * 8);
+  const int64_t* h_pair = (const int64_t*)(stage + (size_t)(2 * E + LC_N) * 8);
 
   const int64_t A = routes_of(cfg);
   const int64_t be = elem_bytes(cfg);
@@ -264,6 +320,25 @@ int moe_ledger(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_ga
   else if (h_cnt[LC_INVALID_RANK] > 0) L.status = MOE_ERR_INVALID_ARG;
   *out = L;
   return L.status;
+}
+
+
+int moe_ledger(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_gate,
+               const int32_t* route_row, int64_t capacity, const int32_t* src_rank,
+               const int32_t* owner_rank, int32_t n_ep, double alpha, moe_ledger_t* out,
+               int64_t* loads, double* f, double* P, int64_t* pair_routes, void* ws,
+               size_t ws_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!out || capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (n_ep < 1 || n_ep > kMaxRanks) return MOE_ERR_INVALID_ARG;
+  std::vector<char> stage(ledger_final_bytes(cfg->E, n_ep));
+  st = moe_ledger_launch(cfg, topk_idx, topk_gate, route_row, src_rank, owner_rank, n_ep,
+                         stage.data(), stage.size(), ws, ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
+  return moe_ledger_finalize(cfg, capacity, n_ep, alpha, stage.data(), out, loads, f, P,
+                             pair_routes);
 }
 
 }  // extern "C"

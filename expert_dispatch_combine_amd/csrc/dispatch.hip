@@ -172,35 +172,29 @@ __global__ __launch_bounds__(256) void slot_kernel(
 
 // x_disp[row] = x[row_token[row]] for row < R = offsets[E]; rows are
 // row_vecs 16-byte vectors long.  Each workgroup moves ROWS rows.
+// All ROWS loads of a column are issued before the stores, so each thread
+// keeps ROWS 16-byte reads in flight.
 template <int ROWS>
-__global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x,
+__global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x,
                                                      const int32_t* __restrict__ row_token,
                                                      const int32_t* __restrict__ offsets,
                                                      int E, int row_vecs,
-                                                     uint4* __restrict__ xd) {
+                                                     u32x4* __restrict__ xd) {
   const int R = offsets[E];
-  const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+  const int r0 = blockIdx.x * ROWS;
   if (r0 >= R) return;
-  const int nrows = (int)min((int64_t)ROWS, (int64_t)R - r0);
-  const int total = nrows * row_vecs;
-  constexpr int U = 4;
-  for (int v0 = threadIdx.x; v0 < total; v0 += 256 * U) {
-    uint4 tmp[U];
-    int64_t dst[U];
+  int64_t src[ROWS];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int v = v0 + u * 256;
-      dst[u] = -1;
-      if (v < total) {
-        const int r = v / row_vecs, c = v % row_vecs;
-        const int t = row_token[r0 + r];
-        tmp[u] = x[(int64_t)t * row_vecs + c];
-        dst[u] = (r0 + r) * row_vecs + c;
-      }
-    }
+  for (int r = 0; r < ROWS; ++r)
+    src[r] = (r0 + r < R) ? (int64_t)row_token[r0 + r] * row_vecs : -1;
+  for (int c = threadIdx.x; c < row_vecs; c += 256) {
+    u32x4 v[ROWS];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (dst[u] >= 0) xd[dst[u]] = tmp[u];
+    for (int r = 0; r < ROWS; ++r)
+      if (src[r] >= 0) v[r] = x[src[r] + c];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+      if (src[r] >= 0) xd[(int64_t)(r0 + r) * row_vecs + c] = v[r];
   }
 }
 
@@ -242,12 +236,12 @@ hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int64_t A, in
                      cap, nb, counts, offsets, route_rank, route_row, row_token, load);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || r_max == 0) return err;
-  if (row_bytes % 16 == 0) {
+  if (row_bytes % 16 == 0 && ((uintptr_t)x & 15u) == 0 && ((uintptr_t)x_disp & 15u) == 0) {
     constexpr int ROWS = 8;
     const int64_t grid = (r_max + ROWS - 1) / ROWS;
     hipLaunchKernelGGL((gather_kernel<ROWS>), dim3((unsigned)grid), dim3(256), 0, s,
-                       (const uint4*)x, row_token, offsets, E, (int)(row_bytes / 16),
-                       (uint4*)x_disp);
+                       (const u32x4*)x, row_token, offsets, E, (int)(row_bytes / 16),
+                       (u32x4*)x_disp);
   } else {
     hipLaunchKernelGGL(gather_bytes_kernel, dim3((unsigned)r_max), dim3(256), 0, s,
                        (const uint8_t*)x, row_token, offsets, E, row_bytes,

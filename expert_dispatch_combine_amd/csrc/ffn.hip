@@ -1,38 +1,53 @@
-// Expert FFN over ragged expert segments: a grouped GEMM on bf16 MFMA.
+// Expert FFN over ragged expert segments: grouped GEMMs on bf16 MFMA.
 //
 // Method: "MoE大模型专家并行与动态路由优化" section 一, FFN(x) = W2 sigma(W1 x + b1)
 // + b2 per expert, sigma = GELU (tanh form).  Each expert e owns the rows
 // [offsets[e], offsets[e+1]) of the dispatched buffer:
 //   GEMM1: H[r, n] = GELU(sum_k x_disp[r, k] W1[e, n, k] + b1[e, n])  -> bf16
 //   GEMM2: Y[r, n] = sum_k H[r, k] W2[e, n, k] + b2[e, n]             -> fp32
-// Both products read the activation rows and the weight rows along the
-// contiguous reduction dimension ("NT" layout), so both operands stream as
-// 16-byte vectors.
+// The MFMA is v_mfma_f32_32x32x16_bf16 with the WEIGHT rows as operand A and
+// the activation rows as operand B: an accumulator lane then holds one
+// activation row and 4 consecutive output columns (8-byte bf16 / 16-byte fp32
+// stores).  Within a 16-wide k-step a lane supplies 8 consecutive k of its
+// row; which 8 is a free choice as long as both operands agree.
 //
-// Kernel shape (gfx950): 256 threads = 4 waves in a 2 x 2 grid, tile
-// BM = 128 rows x BN (128 or 64) weight rows, BK = 64, double-buffered LDS
-// (rows padded by 16 bytes), v_mfma_f32_32x32x16_bf16 with the WEIGHT tile as
-// the MFMA A operand and the activation tile as the B operand, so each
-// accumulator lane holds one activation row and 4 consecutive output columns
-// (8-byte bf16 / 16-byte fp32 stores in the epilogue).
+// Weights come in one of two layouts:
+//  * row-major [E, N, K] as the caller stores them;
+//  * packed (moe_pack_expert_weights): per expert, per 32-row tile, per
+//    64-wide k-chunk, one 4 KB block laid out exactly as a wave's lanes hold
+//    its MFMA fragments -- lane l = (row l%32, half l/32), k-step q holds
+//    k = 32*(l/32) + 8q .. +7 at byte (64 q + l) * 16.  A wave then reads each
+//    fragment as one contiguous 1 KB load and a 32-row strip of a weight as
+//    one linear stream, which is what HBM serves at full rate (row-major
+//    fragments touch 32 rows x 32 bytes per load and run ~30% slower).
+//
+// Two kernel shapes, chosen per launch on the host:
+//  * streaming (rows per expert up to a few hundred: weight-bandwidth bound).
+//    A workgroup takes ALL rows of one expert (up to 160, in 32-row MFMA
+//    tiles) and 32*WN weight rows, so each weight byte crosses HBM once.
+//    Weights go straight from global memory into a register ring PD chunks
+//    deep (no LDS); activations are shared by the 4 waves through a
+//    double-buffered, XOR-swizzled LDS tile, loaded two chunks ahead.  WK
+//    waves split each 64-wide k-chunk when the weight dim is too short to
+//    give the chip enough work; their partial sums are added in LDS in a
+//    fixed order.
+//  * tiled (hundreds of rows per expert: MFMA bound).  128 x BN tiles with
+//    both operands double-buffered in LDS, 4 waves in a 2 x 2 grid.
 //
 // Scheduling is on the device (no host sync): every workgroup derives the
 // per-expert tile counts from `offsets`, maps its id to a logical tile with an
-// XCD-aware permutation (consecutive logical tiles run on the same XCD, so
-// they share its L2), and exits if it has none.  Logical tiles are ordered per
-// expert, then in groups of 8 weight tiles, then row tiles fastest, so tiles
-// that run together share their weight and activation panels.
+// XCD-aware permutation (consecutive logical tiles run on the same XCD and
+// share its L2) and exits if it has none.  Logical tiles are ordered by
+// expert, then groups of 8 weight tiles, then row tiles fastest.
 #include "moe_internal.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int BM = 128;
-constexpr int BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (16-byte pad)
-constexpr int NGROUP = 8;           // weight tiles per scheduling group
-constexpr int NXCD = 8;             // XCDs of an MI355X
+constexpr int NGROUP = 8;  // weight tiles per scheduling group
+constexpr int NXCD = 8;    // XCDs of an MI355X
+constexpr int PBLK = 2048; // bf16 elements of one packed block (32 rows x 64 k)
 
 __device__ __forceinline__ float gelu_tanh_f(float u) {
   // 0.5 u (1 + tanh(z)) == u * sigmoid(2 z),  z = sqrt(2/pi) (u + 0.044715 u^3)
@@ -44,13 +59,14 @@ struct TileInfo {
   int e, row0, row_end, n0;
 };
 
-// Find this workgroup's tile.  Returns false if it has none.
-template <int BN>
+// Find this workgroup's (expert, row tile, weight tile).  False: no tile.
+template <int BM, int BN>
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int N,
                                           TileInfo* sh, int tid) {
   const int ntn = N / BN;
   if (tid < 64) {
     const int lane = tid;
+    if (lane == 0) sh->e = -1;
     const int per = (E + 63) / 64;
     const int ebeg = min(E, lane * per), eend = min(E, ebeg + per);
     int mine = 0;
@@ -70,7 +86,6 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
     int L = -1;
     if (bid < per_xcd * NXCD) L = (bid % NXCD) * per_xcd + bid / NXCD;
     if (L >= total) L = -1;
-    if (lane == 0) sh->e = -1;
     if (L >= 0) {
       int p = incl - mine;
       for (int e = ebeg; e < eend; ++e) {
@@ -96,28 +111,240 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
   return sh->e >= 0;
 }
 
-// EPI 0: out = bf16(GELU(acc + bias)),  EPI 1: out = fp32(acc + bias)
-template <int BN, int EPI>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_bf16_kernel(
+// Epilogue of one 32x32 accumulator: lane holds row m and, for q = 0..3,
+// columns n + 8q .. n + 8q + 3.  EPI 0: bf16(GELU(acc + b)), EPI 1: acc + b.
+template <int EPI>
+__device__ __forceinline__ void store_tile(const f32x16& acc, const float* __restrict__ bptr,
+                                           void* __restrict__ out, int m, int n, int N) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int nn = n + q * 8;
+    const float4 b = *(const float4*)(bptr + nn);
+    float v0 = acc[4 * q + 0] + b.x;
+    float v1 = acc[4 * q + 1] + b.y;
+    float v2 = acc[4 * q + 2] + b.z;
+    float v3 = acc[4 * q + 3] + b.w;
+    if (EPI == 0) {
+      uint2 pk;
+      pk.x = f32_to_bf16_bits(gelu_tanh_f(v0)) | (f32_to_bf16_bits(gelu_tanh_f(v1)) << 16);
+      pk.y = f32_to_bf16_bits(gelu_tanh_f(v2)) | (f32_to_bf16_bits(gelu_tanh_f(v3)) << 16);
+      *(uint2*)((uint16_t*)out + (size_t)m * N + nn) = pk;
+    } else {
+      *(float4*)((float*)out + (size_t)m * N + nn) = make_float4(v0, v1, v2, v3);
+    }
+  }
+}
+
+// Activation LDS tile: rows of 64 bf16 (8 quads); quad q of row r is stored at
+// quad q ^ ((r >> 1) & 7).  Two consecutive rows share one 256-byte bank
+// window, so this spreads any 16 consecutive rows read at one quad over all
+// 16 bank groups (conflict-free ds_read_b128).
+__device__ __forceinline__ int act_slot(int r, int q) { return r * 64 + ((q ^ ((r >> 1) & 7)) << 3); }
+
+// ==========================================================================
+// streaming kernel
+// ==========================================================================
+template <int MT, int WN, int WK>
+struct StreamShape {
+  static constexpr int BM = 32 * MT;         // activation rows per workgroup
+  static constexpr int BN = 32 * WN;         // weight rows per workgroup
+  static constexpr int KC = 64;              // k per chunk (one LDS stage)
+  static constexpr int KW = KC / WK;         // k per wave and chunk
+  static constexpr int KSTEPS = KW / 16;     // MFMA k-steps per wave and chunk
+  // chunks in the weight ring: 16 KB in flight per wave (8 KB when a wave
+  // takes only 16 k of a chunk, to stay within the register budget)
+  static constexpr int PD = (256 / KW) < 8 ? (256 / KW) : 8;
+  static constexpr int STAGE = BM * KC;      // bf16 elements of one LDS stage
+  static constexpr int ACT_BYTES = 2 * STAGE * 2;
+  static constexpr int RED_BYTES = (WK - 1) * WN * MT * 16 * 64 * 4;
+  static constexpr int LDS_BYTES = ACT_BYTES > RED_BYTES ? ACT_BYTES : RED_BYTES;
+};
+
+template <int MT, int WN, int WK, int EPI, bool PK>
+__global__ __launch_bounds__(256, 2) void stream_gemm_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+    const float* __restrict__ bias, void* __restrict__ out,
+    const int32_t* __restrict__ offsets, int E, int N, int Kd) {
+  using S = StreamShape<MT, WN, WK>;
+  __shared__ __attribute__((aligned(16))) char lds[S::LDS_BYTES];
+  __shared__ TileInfo tinfo;
+  uint16_t* act = (uint16_t*)lds;  // [2][BM rows][8 quads], swizzled
+
+  const int tid = threadIdx.x;
+  if (!find_tile<S::BM, S::BN>(offsets, E, N, &tinfo, tid)) return;
+  const int e = tinfo.e, row0 = tinfo.row0, row_end = tinfo.row_end, n0 = tinfo.n0;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % WN, kw = wave / WN;
+  const int li = lane & 31, lg = lane >> 5;
+  const int nchunks = Kd / S::KC;
+
+  // ---- weights: base of this lane's fragments; chunk c / k-step s adds
+  //      c * CSTR + s * QSTR
+  const uint16_t* wp;
+  constexpr int CSTR = PK ? PBLK : S::KC;
+  constexpr int QSTR = PK ? 512 : 8;
+  if (PK)
+    wp = W + ((size_t)e * (N / 32) + (n0 + wn * 32) / 32) * nchunks * PBLK +
+         (kw * S::KSTEPS * 64 + lane) * 8;
+  else
+    wp = W + ((size_t)e * N + n0 + wn * 32 + li) * Kd + kw * S::KW + lg * (S::KW / 2);
+  // ---- activations: this thread stages MT quads per chunk (row c/8, quad c%8)
+  const uint16_t* ap[MT];
+  int alds[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int c = tid + 256 * j;
+    const int r = c >> 3, q = c & 7;
+    const int row = min(row0 + r, row_end - 1);
+    ap[j] = A + (size_t)row * Kd + q * 8;
+    alds[j] = act_slot(r, q);
+  }
+  // activation fragments: the quad of the chunk that matches the weights' k
+  int afrag[MT][S::KSTEPS];
+#pragma unroll
+  for (int tm = 0; tm < MT; ++tm)
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; ++s) {
+      const int r = tm * 32 + li;
+      const int q = PK ? lg * 4 + kw * S::KSTEPS + s
+                       : (kw * S::KW + lg * (S::KW / 2) + s * 8) >> 3;
+      afrag[tm][s] = act_slot(r, q);
+    }
+
+  f32x16 acc[MT];
+#pragma unroll
+  for (int tm = 0; tm < MT; ++tm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[tm][r] = 0.f;
+
+  u32x4 wr[S::PD][S::KSTEPS];
+#pragma unroll
+  for (int p = 0; p < S::PD; ++p)
+    if (p < nchunks)
+#pragma unroll
+      for (int q = 0; q < S::KSTEPS; ++q) wr[p][q] = *(const u32x4*)(wp + p * CSTR + q * QSTR);
+
+  // activations: chunk 0 straight into LDS stage 0, chunk 1 into register
+  // slot 1; chunk c+2 is always in flight while chunk c is computed
+  u32x4 areg[2][MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) areg[0][j] = *(const u32x4*)(ap[j]);
+  if (nchunks > 1) {
+#pragma unroll
+    for (int j = 0; j < MT; ++j) areg[1][j] = *(const u32x4*)(ap[j] + S::KC);
+  }
+#pragma unroll
+  for (int j = 0; j < MT; ++j) *(u32x4*)(act + alds[j]) = areg[0][j];
+  __syncthreads();
+
+  // One k-chunk c (PD and the stage count are even, so slots are compile-time):
+  // issue the activations of chunk c+2, MFMAs on chunk c (weights from ring
+  // slot SLOT, activations from LDS stage STG), refill the slot with chunk
+  // c+PD, stage chunk c+1 (loaded a chunk earlier) into the other LDS buffer.
+  // In the steady-state loop every condition is compile-time true, so the
+  // body has no branches and the compiler counts the loads in flight exactly.
+#define MOE_STREAM_CHUNK(SLOT, STG, c, HAS_NEXT, HAS_NEXT2, REFILL)                     \
+  do {                                                                                \
+    const uint16_t* stage_ = act + (STG) * S::STAGE;                                  \
+    if (HAS_NEXT2) {                                                                  \
+      _Pragma("unroll") for (int j = 0; j < MT; ++j) areg[STG][j] =                   \
+          *(const u32x4*)(ap[j] + ((c) + 2) * S::KC);                                 \
+    }                                                                                 \
+    _Pragma("unroll") for (int s = 0; s < S::KSTEPS; ++s) {                           \
+      const bf16x8 wa = __builtin_bit_cast(bf16x8, wr[SLOT][s]);                      \
+      _Pragma("unroll") for (int tm = 0; tm < MT; ++tm) {                             \
+        const bf16x8 xb = *(const bf16x8*)(stage_ + afrag[tm][s]);                    \
+        acc[tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, xb, acc[tm], 0, 0, 0);  \
+      }                                                                               \
+    }                                                                                 \
+    if (REFILL) {                                                                     \
+      _Pragma("unroll") for (int q = 0; q < S::KSTEPS; ++q) wr[SLOT][q] =             \
+          *(const u32x4*)(wp + ((c) + S::PD) * CSTR + q * QSTR);                      \
+    }                                                                                 \
+    if (HAS_NEXT) {                                                                   \
+      uint16_t* nst_ = act + ((STG) ^ 1) * S::STAGE;                                  \
+      _Pragma("unroll") for (int j = 0; j < MT; ++j) *(u32x4*)(nst_ + alds[j]) =      \
+          areg[(STG) ^ 1][j];                                                         \
+    }                                                                                 \
+    __syncthreads();                                                                  \
+  } while (0)
+
+  // steady state: chunks c+1, c+2 and c+PD all exist
+  int c0 = 0;
+  for (; c0 + 2 * S::PD <= nchunks; c0 += S::PD) {
+#pragma unroll
+    for (int p = 0; p < S::PD; ++p) MOE_STREAM_CHUNK(p, p & 1, c0 + p, true, true, true);
+  }
+  // tail: the last (fewer than 2*PD) chunks
+#pragma unroll
+  for (int p = 0; p < 2 * S::PD; ++p) {
+    const int c = c0 + p;
+    if (c < nchunks)
+      MOE_STREAM_CHUNK(p % S::PD, p & 1, c, c + 1 < nchunks, c + 2 < nchunks,
+                       c + S::PD < nchunks);
+  }
+#undef MOE_STREAM_CHUNK
+
+  // ---- k-split waves: add partial sums in wave order through LDS
+  if (WK > 1) {
+    float* red = (float*)lds;
+    if (kw > 0) {
+#pragma unroll
+      for (int tm = 0; tm < MT; ++tm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          red[((((kw - 1) * WN + wn) * MT + tm) * 16 + r) * 64 + lane] = acc[tm][r];
+    }
+    __syncthreads();
+    if (kw > 0) return;
+#pragma unroll
+    for (int k2 = 1; k2 < WK; ++k2)
+#pragma unroll
+      for (int tm = 0; tm < MT; ++tm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[tm][r] += red[((((k2 - 1) * WN + wn) * MT + tm) * 16 + r) * 64 + lane];
+  }
+
+  const float* bptr = bias + (size_t)e * N;
+  const int n = n0 + wn * 32 + lg * 4;
+#pragma unroll
+  for (int tm = 0; tm < MT; ++tm) {
+    const int m = row0 + tm * 32 + li;
+    if (m < row_end) store_tile<EPI>(acc[tm], bptr, out, m, n, N);
+  }
+}
+
+// ==========================================================================
+// tiled kernel (both operands in LDS)
+// ==========================================================================
+constexpr int TBM = 128;
+constexpr int TBK = 64;
+constexpr int TLDS = TBK + 8;  // bf16 elements per padded LDS row (16-byte pad)
+
+template <int BN, int EPI, bool PK>
+__global__ __launch_bounds__(256, 2) void tiled_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, void* __restrict__ out,
     const int32_t* __restrict__ offsets, int E, int N, int Kd) {
   constexpr int TM = 2;        // 32-row MFMA tiles per wave (wave covers 64 rows)
   constexpr int TN = BN / 64;  // 32-col MFMA tiles per wave (wave covers BN/2 cols)
-  constexpr int ACH = BM * BK / 8 / 256;  // 16-byte chunks per thread per stage (A)
-  constexpr int WCH = BN * BK / 8 / 256;  // (W)
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * LDS_STRIDE];
+  constexpr int ACH = TBM * TBK / 8 / 256;  // 16-byte chunks per thread per stage (A)
+  constexpr int WCH = BN * TBK / 8 / 256;   // (W)
+  // packed weights need no padding: a block's fragment reads are linear
+  constexpr int WSTAGE = PK ? BN * TBK : BN * TLDS;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][TBM * TLDS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][WSTAGE];
   __shared__ TileInfo tinfo;
 
   const int tid = threadIdx.x;
-  if (!find_tile<BN>(offsets, E, N, &tinfo, tid)) return;
+  if (!find_tile<TBM, BN>(offsets, E, N, &tinfo, tid)) return;
   const int e = tinfo.e, row0 = tinfo.row0, row_end = tinfo.row_end, n0 = tinfo.n0;
 
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
+  const int nk = Kd / TBK;
 
-  // global source pointers of this thread's staging chunks (k offset added per stage)
   const uint16_t* a_src[ACH];
   int a_lds[ACH];
 #pragma unroll
@@ -126,17 +353,24 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16_kernel(
     const int r = c >> 3, cc = c & 7;
     const int row = min(row0 + r, row_end - 1);
     a_src[j] = A + (size_t)row * Kd + cc * 8;
-    a_lds[j] = r * LDS_STRIDE + cc * 8;
+    a_lds[j] = r * TLDS + cc * 8;
   }
+  // weight staging: row-major -> 16-byte chunk (row c/8, quad c%8) of the
+  // tile; packed -> quad `tid` of 32-row block j (one 4 KB block per j)
   const uint16_t* w_src[WCH];
   int w_lds[WCH];
-  const uint16_t* wbase = W + ((size_t)e * N + n0) * Kd;
+  constexpr int WKSTR = PK ? PBLK : TBK;  // element stride of one k-stage
 #pragma unroll
   for (int j = 0; j < WCH; ++j) {
-    const int c = tid + j * 256;
-    const int r = c >> 3, cc = c & 7;
-    w_src[j] = wbase + (size_t)r * Kd + cc * 8;
-    w_lds[j] = r * LDS_STRIDE + cc * 8;
+    if (PK) {
+      w_src[j] = W + ((size_t)e * (N / 32) + n0 / 32 + j) * nk * PBLK + tid * 8;
+      w_lds[j] = j * PBLK + tid * 8;
+    } else {
+      const int c = tid + j * 256;
+      const int r = c >> 3, cc = c & 7;
+      w_src[j] = W + ((size_t)e * N + n0 + r) * Kd + cc * 8;
+      w_lds[j] = r * TLDS + cc * 8;
+    }
   }
 
   f32x16 acc[TM][TN];
@@ -147,47 +381,48 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // fragment offsets inside a stage
-  const int kq = (lane >> 5) * 8;
+  // fragment offsets: k-step kk covers k = kk*16 + 8*(lane/32) (row-major)
+  // or k = 32*(lane/32) + 8*kk (packed); both operands use the same map
+  const int li = lane & 31, lg = lane >> 5;
   int a_frag[TM], w_frag[TN];
+  constexpr int KK_STEP = PK ? 8 : 16;
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) a_frag[tm] = (wm * 64 + tm * 32 + (lane & 31)) * LDS_STRIDE + kq;
+  for (int tm = 0; tm < TM; ++tm)
+    a_frag[tm] = (wm * 64 + tm * 32 + li) * TLDS + (PK ? lg * 32 : lg * 8);
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn)
-    w_frag[tn] = (wn * (BN / 2) + tn * 32 + (lane & 31)) * LDS_STRIDE + kq;
+    w_frag[tn] = PK ? (wn * (BN / 64) + tn) * PBLK + lane * 8
+                    : (wn * (BN / 2) + tn * 32 + li) * TLDS + lg * 8;
+  constexpr int WKK_STEP = PK ? 512 : 16;  // packed: k-step kk is quad kk of the block
 
-  const int nk = Kd / BK;
   u32x4 a_reg[ACH], w_reg[WCH];
-#define MOE_GLOAD(k0)                                                              \
-  do {                                                                             \
-    _Pragma("unroll") for (int j = 0; j < ACH; ++j) a_reg[j] =                     \
-        *(const u32x4*)(a_src[j] + (k0));                                          \
-    _Pragma("unroll") for (int j = 0; j < WCH; ++j) w_reg[j] =                     \
-        *(const u32x4*)(w_src[j] + (k0));                                          \
-  } while (0)
-#define MOE_LSTORE(buf)                                                            \
-  do {                                                                             \
-    _Pragma("unroll") for (int j = 0; j < ACH; ++j)                                \
-        *(u32x4*)(&As[(buf)][a_lds[j]]) = a_reg[j];                                \
-    _Pragma("unroll") for (int j = 0; j < WCH; ++j)                                \
-        *(u32x4*)(&Ws[(buf)][w_lds[j]]) = w_reg[j];                                \
-  } while (0)
-  MOE_GLOAD(0);
-  MOE_LSTORE(0);
+#pragma unroll
+  for (int j = 0; j < ACH; ++j) a_reg[j] = *(const u32x4*)(a_src[j]);
+#pragma unroll
+  for (int j = 0; j < WCH; ++j) w_reg[j] = *(const u32x4*)(w_src[j]);
+#pragma unroll
+  for (int j = 0; j < ACH; ++j) *(u32x4*)(&As[0][a_lds[j]]) = a_reg[j];
+#pragma unroll
+  for (int j = 0; j < WCH; ++j) *(u32x4*)(&Ws[0][w_lds[j]]) = w_reg[j];
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     const bool more = kt + 1 < nk;
-    if (more) MOE_GLOAD((kt + 1) * BK);
+    if (more) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+      for (int j = 0; j < ACH; ++j) a_reg[j] = *(const u32x4*)(a_src[j] + (kt + 1) * TBK);
+#pragma unroll
+      for (int j = 0; j < WCH; ++j) w_reg[j] = *(const u32x4*)(w_src[j] + (kt + 1) * WKSTR);
+    }
+#pragma unroll
+    for (int kk = 0; kk < TBK / 16; ++kk) {
       bf16x8 wf[TN], af[TM];
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
-        wf[tn] = *(const bf16x8*)(&Ws[buf][w_frag[tn] + kk * 16]);
+        wf[tn] = *(const bf16x8*)(&Ws[buf][w_frag[tn] + kk * WKK_STEP]);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
-        af[tm] = *(const bf16x8*)(&As[buf][a_frag[tm] + kk * 16]);
+        af[tm] = *(const bf16x8*)(&As[buf][a_frag[tm] + kk * KK_STEP]);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -195,44 +430,46 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16_kernel(
           acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[tn], af[tm], acc[tm][tn],
                                                                 0, 0, 0);
     }
-    if (more) MOE_LSTORE(buf ^ 1);
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < ACH; ++j) *(u32x4*)(&As[buf ^ 1][a_lds[j]]) = a_reg[j];
+#pragma unroll
+      for (int j = 0; j < WCH; ++j) *(u32x4*)(&Ws[buf ^ 1][w_lds[j]]) = w_reg[j];
+    }
     __syncthreads();
   }
-#undef MOE_GLOAD
-#undef MOE_LSTORE
 
-  // epilogue: lane holds row (lane % 32) of each 32-row tile and, for
-  // g = 0..3, columns 8g + 4*(lane/32) + 0..3 of each 32-col tile
   const float* bptr = bias + (size_t)e * N;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
-    const int m = row0 + wm * 64 + tm * 32 + (lane & 31);
+    const int m = row0 + wm * 64 + tm * 32 + li;
     if (m >= row_end) continue;
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * (BN / 2) + tn * 32 + g * 8 + (lane >> 5) * 4;
-        const float4 b = *(const float4*)(bptr + n);
-        float v0 = acc[tm][tn][4 * g + 0] + b.x;
-        float v1 = acc[tm][tn][4 * g + 1] + b.y;
-        float v2 = acc[tm][tn][4 * g + 2] + b.z;
-        float v3 = acc[tm][tn][4 * g + 3] + b.w;
-        if (EPI == 0) {
-          v0 = gelu_tanh_f(v0);
-          v1 = gelu_tanh_f(v1);
-          v2 = gelu_tanh_f(v2);
-          v3 = gelu_tanh_f(v3);
-          uint2 pk;
-          pk.x = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
-          pk.y = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
-          *(uint2*)((uint16_t*)out + (size_t)m * N + n) = pk;
-        } else {
-          *(float4*)((float*)out + (size_t)m * N + n) = make_float4(v0, v1, v2, v3);
-        }
-      }
-    }
+    for (int tn = 0; tn < TN; ++tn)
+      store_tile<EPI>(acc[tm][tn], bptr, out, m, n0 + wn * (BN / 2) + tn * 32 + lg * 4, N);
   }
+}
+
+// ==========================================================================
+// weight packing: row-major [E, N, K] -> fragment blocks (see file header)
+// ==========================================================================
+__global__ __launch_bounds__(256) void pack_weights_kernel(const u32x4* __restrict__ src,
+                                                           u32x4* __restrict__ dst, int E,
+                                                           int N, int Kd) {
+  const int nchunks = Kd / 64;
+  const int64_t nq = (int64_t)E * N * Kd / 8;   // 16-byte quads
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= nq) return;
+  const int64_t blk = p >> 8;                   // 256 quads per block
+  const int w = (int)(p & 255);
+  const int q = w >> 6, l = w & 63;
+  const int c = (int)(blk % nchunks);
+  const int64_t t = blk / nchunks;              // e * (N/32) + 32-row tile
+  const int nt = (int)(t % (N / 32));
+  const int e = (int)(t / (N / 32));
+  const int n = nt * 32 + (l & 31);
+  const int k = c * 64 + (l >> 5) * 32 + q * 8;
+  dst[p] = src[(((int64_t)e * N + n) * Kd + k) >> 3];
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -267,41 +504,119 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
   out[(size_t)row * N + n] = (EPI == 0) ? gelu_tanh_f(acc) : acc;
 }
 
-template <int BN, int EPI>
-hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
-                       const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
-                       hipStream_t s) {
-  // upper bound of the tile count: sum_e ceil(rows_e / BM) <= r_max / BM + E
-  const int64_t mt = r_max / BM + E;
-  int64_t grid = mt * (N / BN);
-  grid = (grid + NXCD - 1) / NXCD * NXCD;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BN, EPI>), dim3((unsigned)grid), dim3(256), 0,
-                     s, A, W, bias, out, offsets, E, N, Kd);
+// ---------------------------------------------------------------- launchers
+// Upper bound of the tile count: sum_e ceil(rows_e / BM) <= r_max / BM + E,
+// rounded up to whole XCD rounds.
+int64_t grid_for(int64_t r_max, int BM, int E, int N, int BN) {
+  int64_t g = (r_max / BM + E) * (N / BN);
+  return (g + NXCD - 1) / NXCD * NXCD;
+}
+
+template <int MT, int WN, int WK, int EPI, bool PK>
+hipError_t launch_stream(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
+                         const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
+                         hipStream_t s) {
+  const int64_t grid = grid_for(r_max, 32 * MT, E, N, 32 * WN);
+  hipLaunchKernelGGL((stream_gemm_kernel<MT, WN, WK, EPI, PK>), dim3((unsigned)grid),
+                     dim3(256), 0, s, A, W, bias, out, offsets, E, N, Kd);
   return hipGetLastError();
 }
 
-// Weight-tile width: 128 when that already gives the chip (256 CUs x 2
-// workgroups) enough tiles, else 64.
-template <int EPI>
-hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* bias,
+template <int MT, int EPI, bool PK>
+hipError_t launch_stream_mt(int wn, const uint16_t* A, const uint16_t* W, const float* bias,
                             void* out, const int32_t* offsets, int E, int N, int Kd,
                             int64_t r_max, hipStream_t s) {
-  const int64_t est_tiles_128 = ((r_max + BM - 1) / BM) * (N / 128);
-  if (N % 128 == 0 && est_tiles_128 >= 512)
-    return launch_gemm<128, EPI>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
-  return launch_gemm<64, EPI>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+  if (wn == 4)
+    return launch_stream<MT, 4, 1, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+  // the 4-way k split keeps MT <= 3 (its reduction and ring outgrow the registers)
+  if (wn == 2 || MT >= 4)
+    return launch_stream<MT, 2, 2, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+  if constexpr (MT < 4)
+    return launch_stream<MT, 1, 4, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+  return hipErrorInvalidValue;
+}
+
+template <int BN, int EPI, bool PK>
+hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
+                        const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
+                        hipStream_t s) {
+  const int64_t grid = grid_for(r_max, TBM, E, N, BN);
+  hipLaunchKernelGGL((tiled_gemm_kernel<BN, EPI, PK>), dim3((unsigned)grid), dim3(256), 0, s,
+                     A, W, bias, out, offsets, E, N, Kd);
+  return hipGetLastError();
+}
+
+// Shape choice.  rows_typ = the rows a typical expert holds, min(capacity,
+// ceil(A/E)); rows_max = min(capacity, A) bounds every expert.
+//  - rows_typ >= 384: the product is MFMA bound -> tiled 128 x BN kernel.
+//  - else streaming, with the row tile covering every expert's rows when
+//    rows_max <= 160 (each weight byte read once), else 128-row tiles; the
+//    weight-tile width 32*WN is the widest that still gives >= 256
+//    workgroups (one per CU), narrower ones split the k-chunk across waves.
+template <int EPI, bool PK>
+hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* bias,
+                            void* out, const int32_t* offsets, int E, int N, int Kd,
+                            int64_t r_max, int64_t rows_typ, int64_t rows_max,
+                            hipStream_t s) {
+  if (rows_typ >= 384) {
+    const int64_t est = (r_max / TBM) * (N / 128);
+    if (N % 128 == 0 && est >= 512)
+      return launch_tiled<128, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+    return launch_tiled<64, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+  }
+  int mt = (int)((rows_max + 31) / 32);
+  if (mt > 5) mt = 4;
+  if (mt < 1) mt = 1;
+  const int64_t bm = 32 * mt;
+  const int64_t mtiles = (r_max + bm - 1) / bm > E ? (r_max + bm - 1) / bm : E;
+  int wn = 1;
+  if (N % 128 == 0 && mtiles * (N / 128) >= 256) wn = 4;
+  else if (mtiles * (N / 64) >= 256 || mt >= 4) wn = 2;
+  switch (mt) {
+    case 1: return launch_stream_mt<1, EPI, PK>(wn, A, W, bias, out, offsets, E, N, Kd, r_max, s);
+    case 2: return launch_stream_mt<2, EPI, PK>(wn, A, W, bias, out, offsets, E, N, Kd, r_max, s);
+    case 3: return launch_stream_mt<3, EPI, PK>(wn, A, W, bias, out, offsets, E, N, Kd, r_max, s);
+    case 4: return launch_stream_mt<4, EPI, PK>(wn, A, W, bias, out, offsets, E, N, Kd, r_max, s);
+    default: return launch_stream_mt<5, EPI, PK>(wn, A, W, bias, out, offsets, E, N, Kd, r_max, s);
+  }
+}
+
+template <bool PK>
+hipError_t launch_ffn_bf16_t(const uint16_t* xd, const int32_t* offsets, const uint16_t* w1,
+                             const float* b1, const uint16_t* w2, const float* b2,
+                             uint16_t* hbuf, float* y, int E, int h, int F, int64_t A,
+                             int64_t cap, int64_t r_max, hipStream_t s) {
+  if (r_max == 0) return hipSuccess;
+  const int64_t avg = (A + E - 1) / E;
+  const int64_t rows_typ = avg < cap ? avg : cap;
+  const int64_t rows_max = A < cap ? A : cap;
+  hipError_t err = launch_gemm_auto<0, PK>(xd, w1, b1, hbuf, offsets, E, F, h, r_max, rows_typ,
+                                           rows_max, s);
+  if (err != hipSuccess) return err;
+  return launch_gemm_auto<1, PK>(hbuf, w2, b2, y, offsets, E, h, F, r_max, rows_typ, rows_max,
+                                 s);
 }
 
 }  // namespace
 
 hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* offsets, const uint16_t* w1,
                            const float* b1, const uint16_t* w2, const float* b2,
-                           uint16_t* hbuf, float* y, int E, int h, int F, int64_t r_max,
-                           hipStream_t s) {
-  if (r_max == 0) return hipSuccess;
-  hipError_t err = launch_gemm_auto<0>(xd, w1, b1, hbuf, offsets, E, F, h, r_max, s);
-  if (err != hipSuccess) return err;
-  return launch_gemm_auto<1>(hbuf, w2, b2, y, offsets, E, h, F, r_max, s);
+                           uint16_t* hbuf, float* y, int E, int h, int F, int64_t A,
+                           int64_t cap, int64_t r_max, bool packed, hipStream_t s) {
+  if (packed)
+    return launch_ffn_bf16_t<true>(xd, offsets, w1, b1, w2, b2, hbuf, y, E, h, F, A, cap,
+                                   r_max, s);
+  return launch_ffn_bf16_t<false>(xd, offsets, w1, b1, w2, b2, hbuf, y, E, h, F, A, cap, r_max,
+                                  s);
+}
+
+hipError_t launch_pack_weights(const uint16_t* w, uint16_t* wp, int E, int N, int Kd,
+                               hipStream_t s) {
+  const int64_t nq = (int64_t)E * N * Kd / 8;
+  if (nq == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s,
+                     (const u32x4*)w, (u32x4*)wp, E, N, Kd);
+  return hipGetLastError();
 }
 
 hipError_t launch_ffn_f32(const float* xd, const int32_t* offsets, const float* w1,

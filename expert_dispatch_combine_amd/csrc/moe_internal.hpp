@@ -17,7 +17,7 @@ constexpr int kMaxRanks = 64;
 // Routes handled by one workgroup of the dispatch count / slot kernels.
 constexpr int kDispatchRoutesPerBlock = 1024;
 // Routes handled by one workgroup of the ledger partial kernel.
-constexpr int kLedgerRoutesPerBlock = 2048;
+constexpr int kLedgerRoutesPerBlock = 512;
 // Scalar counters of the ledger, per block and in the final area.
 enum LedgerCounter {
   LC_LOCAL_ALL = 0,
@@ -55,6 +55,10 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // from offset 0; regions of different calls may overlap).
 size_t dispatch_ws_bytes(int64_t A, int E);
 size_t ledger_ws_bytes(int64_t A, int E, int n_ep);
+// Bytes of the ledger's compact result (device final area == host stage).
+inline size_t ledger_final_bytes(int E, int n_ep) {
+  return (size_t)(2 * E + LC_N + n_ep * n_ep) * 8;
+}
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the first HIP error.
@@ -78,8 +82,11 @@ hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int64_t A, in
 
 hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* offsets, const uint16_t* w1,
                            const float* b1, const uint16_t* w2, const float* b2,
-                           uint16_t* hbuf, float* y, int E, int h, int F, int64_t r_max,
-                           hipStream_t s);
+                           uint16_t* hbuf, float* y, int E, int h, int F, int64_t A,
+                           int64_t cap, int64_t r_max, bool packed, hipStream_t s);
+// Row-major [E, N, K] bf16 -> packed fragment blocks (N % 32 == 0, K % 64 == 0).
+hipError_t launch_pack_weights(const uint16_t* w, uint16_t* wp, int E, int N, int Kd,
+                               hipStream_t s);
 hipError_t launch_ffn_f32(const float* xd, const int32_t* offsets, const float* w1,
                           const float* b1, const float* w2, const float* b2, float* hbuf,
                           float* y, int E, int h, int F, int64_t r_max, hipStream_t s);

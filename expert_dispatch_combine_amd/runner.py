@@ -1,17 +1,22 @@
 """Device buffers for one MoE layer and the call sequence of the C ABI.
 
-`LayerBuffers` allocates every output/scratch tensor the five entry points
-need (sizes from moe_max_rows / moe_workspace_bytes); `run_layer` issues
+`LayerBuffers` allocates every output/scratch tensor the entry points need
+(sizes from moe_max_rows / moe_workspace_bytes); `run_layer` issues
 moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine on one stream.
-No arithmetic of the method happens here.
+`LayerPlan` marshals the same calls once for fixed tensors and a fixed stream,
+so a serving loop (or a HIP-graph capture) pays only the bare C calls per
+step.  No arithmetic of the method happens here.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
-from ._binding import (MOE_BF16, MoeCfg, moe_capacity, moe_combine, moe_dispatch,
-                       moe_expert_ffn, moe_ledger, moe_max_rows, moe_route,
-                       moe_workspace_bytes)
+from ._binding import (MOE_BF16, MoeCfg, MoeError, _ptr, _ws, load_library, moe_capacity,
+                       moe_combine, moe_dispatch, moe_expert_ffn, moe_expert_ffn_packed,
+                       moe_ledger, moe_ledger_finalize, moe_ledger_stage_bytes, moe_max_rows,
+                       moe_pack_expert_weights, moe_route, moe_workspace_bytes)
 
 
 class LayerBuffers:
@@ -58,9 +63,16 @@ def run_dispatch(b: LayerBuffers, x, expert_load=False, stream=None):
                  b.row_token, b.x_disp, b.expert_load if expert_load else None, b.ws, stream)
 
 
-def run_ffn(b: LayerBuffers, w1, b1, w2, b2, stream=None):
-    moe_expert_ffn(b.cfg, b.capacity, b.x_disp, b.expert_offsets, w1, b1, w2, b2, b.h_buf, b.y,
-                   stream)
+def run_ffn(b: LayerBuffers, w1, b1, w2, b2, stream=None, packed=False):
+    fn = moe_expert_ffn_packed if packed else moe_expert_ffn
+    fn(b.cfg, b.capacity, b.x_disp, b.expert_offsets, w1, b1, w2, b2, b.h_buf, b.y, stream)
+
+
+def pack_weights(cfg: MoeCfg, w1, w2, stream=None):
+    """Packed copies of W1 and W2 (moe_pack_expert_weights)."""
+    w1p, w2p = torch.empty_like(w1), torch.empty_like(w2)
+    moe_pack_expert_weights(cfg, w1, w2, w1p, w2p, stream)
+    return w1p, w2p
 
 
 def run_combine(b: LayerBuffers, stream=None):
@@ -72,9 +84,111 @@ def run_ledger(b: LayerBuffers, src_rank, owner_rank, n_ep, alpha=0.01, stream=N
                       owner_rank, n_ep, alpha, b.ws, stream, **kw)
 
 
-def run_layer(b: LayerBuffers, x, w_gate, logit_bias, w1, b1, w2, b2, stream=None):
-    """route -> dispatch -> expert FFN -> combine (asynchronous on `stream`)."""
+def run_layer(b: LayerBuffers, x, w_gate, logit_bias, w1, b1, w2, b2, stream=None,
+              packed=False):
+    """route -> dispatch -> expert FFN -> combine (asynchronous on `stream`);
+    `packed`: w1/w2 are in the packed fragment layout."""
     run_route(b, x, w_gate, logit_bias, expert_load=False, stream=stream)
     run_dispatch(b, x, expert_load=True, stream=stream)
-    run_ffn(b, w1, b1, w2, b2, stream=stream)
+    run_ffn(b, w1, b1, w2, b2, stream=stream, packed=packed)
     run_combine(b, stream=stream)
+
+
+class LayerPlan:
+    """The whole step -- route, dispatch, expert FFN, combine, and the ledger's
+    device half with the copy of its counters to a page-locked host stage --
+    marshalled once.  `launch()` enqueues it with bare C calls; the ledger
+    runs on `side` (after the dispatch, beside the FFN) when given, joined back
+    into `main` before launch() returns.  After the work has completed,
+    `ledger()` decodes the stage on the host.
+
+    The plan does not own the tensors: they must outlive it and keep their
+    storage (a HIP graph captured from launch() replays these addresses)."""
+
+    def __init__(self, b: LayerBuffers, x, w_gate, logit_bias, w1, b1, w2, b2, src_rank,
+                 owner_rank, n_ep: int, alpha: float = 0.01, main=None, side=None,
+                 ledger_ws=None, packed: bool = False):
+        lib = load_library()
+        cfg = b.cfg
+        self.b, self.cfg, self.n_ep, self.alpha = b, cfg, int(n_ep), float(alpha)
+        self.main = main if main is not None else torch.cuda.current_stream()
+        self.side = side
+        self.stage = torch.empty((moe_ledger_stage_bytes(cfg, n_ep),), dtype=torch.uint8,
+                                 pin_memory=True)
+        self.ledger_ws = ledger_ws if ledger_ws is not None else (
+            torch.empty_like(b.ws) if side is not None else b.ws)
+        ms = ctypes.c_void_p(self.main.cuda_stream)
+        ls = ctypes.c_void_p((side or self.main).cuda_stream)
+        c = ctypes.byref(cfg)
+        wsp, wsb = _ws(b.ws)
+        lwsp, lwsb = _ws(self.ledger_ws)
+        self._cfg_ref = cfg  # byref() keeps no reference of its own
+        self._keep = (x, w_gate, logit_bias, w1, b1, w2, b2, src_rank, owner_rank)
+        p = lambda t, k, n: _ptr(t, k, cfg, n)  # noqa: E731
+        self.route = (lib.moe_route, (c, p(x, "act", "x"), p(w_gate, "act", "w_gate"),
+                                      p(logit_bias, "f32", "logit_bias"),
+                                      p(b.logits, "f32", "logits"),
+                                      p(b.topk_idx, "i32", "topk_idx"),
+                                      p(b.topk_gate, "f32", "topk_gate"), None, wsp, wsb, ms))
+        self.dispatch = (lib.moe_dispatch, (c, p(x, "act", "x"), p(b.topk_idx, "i32", "topk_idx"),
+                                            b.capacity, p(b.expert_offsets, "i32", "offsets"),
+                                            p(b.route_rank, "i32", "route_rank"),
+                                            p(b.route_row, "i32", "route_row"),
+                                            p(b.row_token, "i32", "row_token"),
+                                            p(b.x_disp, "act", "x_disp"),
+                                            p(b.expert_load, "i32", "expert_load"), wsp, wsb, ms))
+        ffn_fn = lib.moe_expert_ffn_packed if packed else lib.moe_expert_ffn
+        self.ffn = (ffn_fn, (c, b.capacity, p(b.x_disp, "act", "x_disp"),
+                                         p(b.expert_offsets, "i32", "offsets"),
+                                         p(w1, "act", "w1"), p(b1, "f32", "b1"),
+                                         p(w2, "act", "w2"), p(b2, "f32", "b2"),
+                                         p(b.h_buf, "act", "h_buf"), p(b.y, "f32", "y"), ms))
+        self.combine = (lib.moe_combine, (c, p(b.y, "f32", "y"), p(b.route_row, "i32", "route_row"),
+                                          p(b.topk_gate, "f32", "topk_gate"),
+                                          p(b.out, "f32", "out"), ms))
+        self.ledger_launch = (lib.moe_ledger_launch, (
+            c, p(b.topk_idx, "i32", "topk_idx"), p(b.topk_gate, "f32", "topk_gate"),
+            p(b.route_row, "i32", "route_row"), p(src_rank, "i32", "src_rank"),
+            p(owner_rank, "i32", "owner_rank"), self.n_ep,
+            ctypes.c_void_p(self.stage.data_ptr()), self.stage.numel(), lwsp, lwsb, ls))
+        self.ev_dispatched = torch.cuda.Event()
+        self.ev_ledger = torch.cuda.Event()
+
+    @staticmethod
+    def _call(name, fa):
+        st = fa[0](*fa[1])
+        if st != 0:
+            raise MoeError(name, st)
+
+    def launch(self, events=None):
+        """Enqueue one step.  `events` (optional, 5 timing events) are recorded
+        on the main stream before route / dispatch / FFN / combine and after."""
+        m = self.main
+        if events:
+            events[0].record(m)
+        self._call("moe_route", self.route)
+        if events:
+            events[1].record(m)
+        self._call("moe_dispatch", self.dispatch)
+        if events:
+            events[2].record(m)
+        if self.side is not None:
+            self.ev_dispatched.record(m)
+            self.side.wait_event(self.ev_dispatched)
+            self._call("moe_ledger_launch", self.ledger_launch)
+            self.ev_ledger.record(self.side)
+        self._call("moe_expert_ffn", self.ffn)
+        if events:
+            events[3].record(m)
+        self._call("moe_combine", self.combine)
+        if events:
+            events[4].record(m)
+        if self.side is None:
+            self._call("moe_ledger_launch", self.ledger_launch)
+        else:
+            m.wait_event(self.ev_ledger)
+
+    def ledger(self, **kw) -> dict:
+        """Decode the host stage (the step's work must have completed)."""
+        return moe_ledger_finalize(self.cfg, self.b.capacity, self.n_ep, self.alpha, self.stage,
+                                   **kw)

@@ -166,6 +166,26 @@ int moe_expert_ffn(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
                    const void* w2, const float* b2, void* h_buf, float* y,
                    void* stream);
 
+/* The same expert FFN on weights in the packed fragment layout produced by
+ * moe_pack_expert_weights (bf16 only).  Expert weights are static, so a
+ * server packs them once at load time; the packed layout lets every wave
+ * read its MFMA operands as contiguous 1 KB loads.  Arguments and results
+ * are those of moe_expert_ffn. */
+int moe_expert_ffn_packed(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
+                          const int32_t* expert_offsets, const void* w1_packed,
+                          const float* b1, const void* w2_packed, const float* b2,
+                          void* h_buf, float* y, void* stream);
+
+/* Repack row-major expert weights (bf16) into the fragment layout:
+ * for expert e, 32-row tile t, 64-wide k-chunk c, one 4096-byte block at
+ * index (e * (N/32) + t) * (K/64) + c, whose 16-byte quad (64*q + l) holds
+ * W[e][32t + l%32][64c + 32*(l/32) + 8q .. +7]  (l = 0..63, q = 0..3).
+ * w1 [E, F, h] -> w1_packed (N = F, K = h); w2 [E, h, F] -> w2_packed
+ * (N = h, K = F); same byte size as the input.  Either pair may be NULL.
+ * Output buffers must not alias the inputs.  Asynchronous on `stream`. */
+int moe_pack_expert_weights(const moe_cfg* cfg, const void* w1, const void* w2,
+                            void* w1_packed, void* w2_packed, void* stream);
+
 /* Weighted combine in original token order, without atomics ([EP46]
  * combine_expert_outputs; [EPC] Combine):
  *   out[t] = sum over k = 0..K-1 with route_row[t,k] >= 0 of
@@ -190,6 +210,26 @@ int moe_ledger(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_ga
                const int32_t* owner_rank, int32_t n_ep, double alpha,
                moe_ledger_t* out, int64_t* loads, double* f, double* P,
                int64_t* pair_routes, void* ws, size_t ws_bytes, void* stream);
+
+/* The same ledger in two halves, so that a serving loop (or a captured HIP
+ * graph) never waits on the host:
+ *   moe_ledger_launch  enqueues the counting kernels and an asynchronous copy
+ *                      of the compact counters into `host_stage` (caller's
+ *                      host memory of moe_ledger_stage_bytes(cfg, n_ep) bytes;
+ *                      page-locked memory keeps the copy asynchronous);
+ *   moe_ledger_finalize, once that copy has completed (stream or event
+ *                      synchronisation by the caller), turns the stage into
+ *                      the same outputs as moe_ledger.  Pure host function.
+ * The workspace must not be reused by another call before the copy is done.
+ * moe_ledger_stage_bytes returns 0 for invalid arguments. */
+size_t moe_ledger_stage_bytes(const moe_cfg* cfg, int32_t n_ep);
+int moe_ledger_launch(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_gate,
+                      const int32_t* route_row, const int32_t* src_rank,
+                      const int32_t* owner_rank, int32_t n_ep, void* host_stage,
+                      size_t stage_bytes, void* ws, size_t ws_bytes, void* stream);
+int moe_ledger_finalize(const moe_cfg* cfg, int64_t capacity, int32_t n_ep, double alpha,
+                        const void* host_stage, moe_ledger_t* out, int64_t* loads,
+                        double* f, double* P, int64_t* pair_routes);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,7 @@ import torch
 import expert_dispatch_combine_amd as M
 import moe_workloads as W
 import oracle as O
-from expert_dispatch_combine_amd.runner import LayerBuffers
+from expert_dispatch_combine_amd.runner import LayerBuffers, pack_weights
 from gpu_util import (U32, banner, bias_np, custom_inputs, device_inputs, host, rms, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +35,7 @@ def _oracle_dispatch(inp: W.Inputs):
     return idx, gate, cap, sl
 
 
-def _run_ffn(inp: W.Inputs, cap, sl):
+def _run_ffn(inp: W.Inputs, cap, sl, packed=False):
     cfg = inp.cfg
     mc = M.MoeCfg.make(cfg.T, cfg.h, cfg.E, cfg.K, cfg.F, cfg.dtype, cfg.cf)
     b = LayerBuffers(mc, cap)
@@ -43,9 +43,16 @@ def _run_ffn(inp: W.Inputs, cap, sl):
     if R:
         b.x_disp[:R].copy_(inp.x[torch.from_numpy(sl["row_token"].astype(np.int64)).cuda()])
     b.expert_offsets.copy_(torch.from_numpy(sl["expert_offsets"]))
-    M.moe_expert_ffn(mc, cap, b.x_disp, b.expert_offsets, inp.w1, inp.b1, inp.w2, inp.b2,
-                     b.h_buf, b.y)
-    torch.cuda.synchronize()
+    if packed:
+        w1p, w2p = pack_weights(mc, inp.w1, inp.w2)
+        M.moe_expert_ffn_packed(mc, cap, b.x_disp, b.expert_offsets, w1p, inp.b1, w2p, inp.b2,
+                                b.h_buf, b.y)
+        torch.cuda.synchronize()
+        del w1p, w2p
+    else:
+        M.moe_expert_ffn(mc, cap, b.x_disp, b.expert_offsets, inp.w1, inp.b1, inp.w2, inp.b2,
+                         b.h_buf, b.y)
+        torch.cuda.synchronize()
     return b
 
 
@@ -85,24 +92,25 @@ def _check_rows(inp, sl, b, rows):
         assert rms(Yg[m] - Y) <= 2.0 ** -8 * rms(Y) + 1e-7
 
 
-@pytest.mark.parametrize("cid", [1, 2, 5])
-def test_ffn_full_on_workloads(cid):
-    banner(f"ffn full config {cid}")
+@pytest.mark.parametrize("cid,packed", [(1, False), (2, False), (2, True), (5, False),
+                                        (5, True)])
+def test_ffn_full_on_workloads(cid, packed):
+    banner(f"ffn full config {cid} packed={packed}")
     inp = device_inputs(cid)
     _, _, cap, sl = _oracle_dispatch(inp)
-    b = _run_ffn(inp, cap, sl)
+    b = _run_ffn(inp, cap, sl, packed)
     _check_rows(inp, sl, b, np.arange(sl["R"]))
 
 
-@pytest.mark.parametrize("cid", [3, 4])
-def test_ffn_sampled_rows_full_size(cid):
+@pytest.mark.parametrize("cid,packed", [(3, False), (3, True), (4, False), (4, True)])
+def test_ffn_sampled_rows_full_size(cid, packed):
     """Full-size workloads, launched exactly as the layer launches them;
     a sample of rows (every expert's first and last row, plus random rows)
     is checked against the oracle row by row."""
-    banner(f"ffn sampled config {cid}")
+    banner(f"ffn sampled config {cid} packed={packed}")
     inp = device_inputs(cid)
     _, _, cap, sl = _oracle_dispatch(inp)
-    b = _run_ffn(inp, cap, sl)
+    b = _run_ffn(inp, cap, sl, packed)
     offs = sl["expert_offsets"]
     rng = np.random.default_rng(cid)
     rows = set()
@@ -121,12 +129,13 @@ def test_ffn_sampled_rows_full_size(cid):
                                           (1000, 256, 16, 2, 320, 1.0),
                                           (513, 64, 64, 6, 128, 1.0),
                                           (2500, 192, 3, 1, 448, 1.5)])
-def test_ffn_ragged_segments(T, h, E, K, F, cf):
-    banner(f"ffn ragged T={T} h={h} E={E} K={K} F={F}")
+@pytest.mark.parametrize("packed", [False, True])
+def test_ffn_ragged_segments(T, h, E, K, F, cf, packed):
+    banner(f"ffn ragged T={T} h={h} E={E} K={K} F={F} packed={packed}")
     cfg = W.custom(T=T, h=h, E=E, K=K, F=F, cf=cf, dtype="bf16", seed=T * 7 + F)
     inp = custom_inputs(cfg)
     _, _, cap, sl = _oracle_dispatch(inp)
-    b = _run_ffn(inp, cap, sl)
+    b = _run_ffn(inp, cap, sl, packed)
     _check_rows(inp, sl, b, np.arange(sl["R"]))
 
 
