@@ -55,6 +55,24 @@ __device__ __forceinline__ float gelu_tanh_f(float u) {
   return u / (1.0f + __expf(-2.0f * z));
 }
 
+// The same GELU for a bf16 result: the hardware base-2 exponential and
+// reciprocal (each within a couple of fp32 ulps) replace the IEEE division,
+// far below the bf16 rounding that follows.  -2 z log2(e) = u (k0 + k1 u^2).
+__device__ __forceinline__ float gelu_tanh_bf16(float u) {
+  constexpr float k0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  constexpr float k1 = k0 * 0.044715f;
+  const float t = u * fmaf(k1, u * u, k0);
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 struct TileInfo {
   int e, row0, row_end, n0;
 };
@@ -126,8 +144,8 @@ __device__ __forceinline__ void store_tile(const f32x16& acc, const float* __res
     float v3 = acc[4 * q + 3] + b.w;
     if (EPI == 0) {
       uint2 pk;
-      pk.x = f32_to_bf16_bits(gelu_tanh_f(v0)) | (f32_to_bf16_bits(gelu_tanh_f(v1)) << 16);
-      pk.y = f32_to_bf16_bits(gelu_tanh_f(v2)) | (f32_to_bf16_bits(gelu_tanh_f(v3)) << 16);
+      pk.x = pack_bf16x2(gelu_tanh_bf16(v0), gelu_tanh_bf16(v1));
+      pk.y = pack_bf16x2(gelu_tanh_bf16(v2), gelu_tanh_bf16(v3));
       *(uint2*)((uint16_t*)out + (size_t)m * N + nn) = pk;
     } else {
       *(float4*)((float*)out + (size_t)m * N + nn) = make_float4(v0, v1, v2, v3);
@@ -144,7 +162,10 @@ __device__ __forceinline__ int act_slot(int r, int q) { return r * 64 + ((q ^ ((
 // ==========================================================================
 // streaming kernel
 // ==========================================================================
-template <int MT, int WN, int WK>
+// OCC = workgroups per CU the kernel is built for.  With OCC 1 (launches with
+// at most one workgroup per CU) each wave owns twice the registers, spent on
+// deeper prefetch: 8 weight chunks and 4 activation chunks in flight.
+template <int MT, int WN, int WK, int OCC>
 struct StreamShape {
   static constexpr int BM = 32 * MT;         // activation rows per workgroup
   static constexpr int BN = 32 * WN;         // weight rows per workgroup
@@ -153,19 +174,26 @@ struct StreamShape {
   static constexpr int KSTEPS = KW / 16;     // MFMA k-steps per wave and chunk
   // chunks in the weight ring: 16 KB in flight per wave (8 KB when a wave
   // takes only 16 k of a chunk, to stay within the register budget)
-  static constexpr int PD = (256 / KW) < 8 ? (256 / KW) : 8;
+  static constexpr int PD = OCC == 1 ? 8 : ((256 / KW) < 8 ? (256 / KW) : 8);
+  // activation register slots: chunk c + AD is loaded while chunk c computes
+  static constexpr int AD = OCC == 1 ? 4 : 2;
   static constexpr int STAGE = BM * KC;      // bf16 elements of one LDS stage
   static constexpr int ACT_BYTES = 2 * STAGE * 2;
   static constexpr int RED_BYTES = (WK - 1) * WN * MT * 16 * 64 * 4;
-  static constexpr int LDS_BYTES = ACT_BYTES > RED_BYTES ? ACT_BYTES : RED_BYTES;
+  // epilogue: 32 output rows at a time, rows padded by 16 bytes
+  static constexpr int OUT_ROW_BYTES(int esz) { return BN * esz + 16; }
+  static constexpr int OUT_BYTES = 32 * (BN * 4 + 16);
+  static constexpr int M1 = ACT_BYTES > RED_BYTES ? ACT_BYTES : RED_BYTES;
+  static constexpr int LDS_BYTES = M1 > OUT_BYTES ? M1 : OUT_BYTES;
 };
 
-template <int MT, int WN, int WK, int EPI, bool PK>
-__global__ __launch_bounds__(256, 2) void stream_gemm_kernel(
+template <int MT, int WN, int WK, int EPI, bool PK, int OCC>
+__global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, void* __restrict__ out,
     const int32_t* __restrict__ offsets, int E, int N, int Kd) {
-  using S = StreamShape<MT, WN, WK>;
+  using S = StreamShape<MT, WN, WK, OCC>;
+  static_assert(S::PD % S::AD == 0 && S::PD % 2 == 0, "ring sizes");
   __shared__ __attribute__((aligned(16))) char lds[S::LDS_BYTES];
   __shared__ TileInfo tinfo;
   uint16_t* act = (uint16_t*)lds;  // [2][BM rows][8 quads], swizzled
@@ -224,31 +252,33 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(
 #pragma unroll
       for (int q = 0; q < S::KSTEPS; ++q) wr[p][q] = *(const u32x4*)(wp + p * CSTR + q * QSTR);
 
-  // activations: chunk 0 straight into LDS stage 0, chunk 1 into register
-  // slot 1; chunk c+2 is always in flight while chunk c is computed
-  u32x4 areg[2][MT];
+  // activations: chunk 0 straight into LDS stage 0, chunks 1 .. AD-1 into
+  // register slots; chunk c+AD is always in flight while chunk c is computed
+  u32x4 areg[S::AD][MT];
 #pragma unroll
   for (int j = 0; j < MT; ++j) areg[0][j] = *(const u32x4*)(ap[j]);
-  if (nchunks > 1) {
 #pragma unroll
-    for (int j = 0; j < MT; ++j) areg[1][j] = *(const u32x4*)(ap[j] + S::KC);
-  }
+  for (int a = 1; a < S::AD; ++a)
+    if (a < nchunks)
+#pragma unroll
+      for (int j = 0; j < MT; ++j) areg[a][j] = *(const u32x4*)(ap[j] + a * S::KC);
 #pragma unroll
   for (int j = 0; j < MT; ++j) *(u32x4*)(act + alds[j]) = areg[0][j];
   __syncthreads();
 
-  // One k-chunk c (PD and the stage count are even, so slots are compile-time):
-  // issue the activations of chunk c+2, MFMAs on chunk c (weights from ring
-  // slot SLOT, activations from LDS stage STG), refill the slot with chunk
-  // c+PD, stage chunk c+1 (loaded a chunk earlier) into the other LDS buffer.
-  // In the steady-state loop every condition is compile-time true, so the
-  // body has no branches and the compiler counts the loads in flight exactly.
-#define MOE_STREAM_CHUNK(SLOT, STG, c, HAS_NEXT, HAS_NEXT2, REFILL)                     \
+  // One k-chunk c (PD is a multiple of AD and of 2, so every slot index is
+  // compile-time): issue the activations of chunk c+AD into slot c%AD, MFMAs
+  // on chunk c (weights from ring slot SLOT, activations from LDS stage STG),
+  // refill the weight slot with chunk c+PD, stage chunk c+1 (register slot
+  // (c+1)%AD, loaded AD-1 chunks earlier) into the other LDS buffer.  In the
+  // steady-state loop every condition is compile-time true, so the body has
+  // no branches and the compiler counts the loads in flight exactly.
+#define MOE_STREAM_CHUNK(SLOT, STG, ASLOT, NSLOT, c, HAS_NEXT, HAS_NEXTA, REFILL)      \
   do {                                                                                \
     const uint16_t* stage_ = act + (STG) * S::STAGE;                                  \
-    if (HAS_NEXT2) {                                                                  \
-      _Pragma("unroll") for (int j = 0; j < MT; ++j) areg[STG][j] =                   \
-          *(const u32x4*)(ap[j] + ((c) + 2) * S::KC);                                 \
+    if (HAS_NEXTA) {                                                                  \
+      _Pragma("unroll") for (int j = 0; j < MT; ++j) areg[ASLOT][j] =                 \
+          *(const u32x4*)(ap[j] + ((c) + S::AD) * S::KC);                             \
     }                                                                                 \
     _Pragma("unroll") for (int s = 0; s < S::KSTEPS; ++s) {                           \
       const bf16x8 wa = __builtin_bit_cast(bf16x8, wr[SLOT][s]);                      \
@@ -264,24 +294,25 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(
     if (HAS_NEXT) {                                                                   \
       uint16_t* nst_ = act + ((STG) ^ 1) * S::STAGE;                                  \
       _Pragma("unroll") for (int j = 0; j < MT; ++j) *(u32x4*)(nst_ + alds[j]) =      \
-          areg[(STG) ^ 1][j];                                                         \
+          areg[NSLOT][j];                                                             \
     }                                                                                 \
     __syncthreads();                                                                  \
   } while (0)
 
-  // steady state: chunks c+1, c+2 and c+PD all exist
+  // steady state: chunks c+1, c+AD and c+PD all exist (PD >= AD)
   int c0 = 0;
   for (; c0 + 2 * S::PD <= nchunks; c0 += S::PD) {
 #pragma unroll
-    for (int p = 0; p < S::PD; ++p) MOE_STREAM_CHUNK(p, p & 1, c0 + p, true, true, true);
+    for (int p = 0; p < S::PD; ++p)
+      MOE_STREAM_CHUNK(p, p & 1, p % S::AD, (p + 1) % S::AD, c0 + p, true, true, true);
   }
   // tail: the last (fewer than 2*PD) chunks
 #pragma unroll
   for (int p = 0; p < 2 * S::PD; ++p) {
     const int c = c0 + p;
     if (c < nchunks)
-      MOE_STREAM_CHUNK(p % S::PD, p & 1, c, c + 1 < nchunks, c + 2 < nchunks,
-                       c + S::PD < nchunks);
+      MOE_STREAM_CHUNK(p % S::PD, p & 1, p % S::AD, (p + 1) % S::AD, c, c + 1 < nchunks,
+                       c + S::AD < nchunks, c + S::PD < nchunks);
   }
 #undef MOE_STREAM_CHUNK
 
@@ -296,22 +327,57 @@ __global__ __launch_bounds__(256, 2) void stream_gemm_kernel(
           red[((((kw - 1) * WN + wn) * MT + tm) * 16 + r) * 64 + lane] = acc[tm][r];
     }
     __syncthreads();
-    if (kw > 0) return;
+    if (kw == 0) {
 #pragma unroll
-    for (int k2 = 1; k2 < WK; ++k2)
+      for (int k2 = 1; k2 < WK; ++k2)
 #pragma unroll
-      for (int tm = 0; tm < MT; ++tm)
+        for (int tm = 0; tm < MT; ++tm)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[tm][r] += red[((((k2 - 1) * WN + wn) * MT + tm) * 16 + r) * 64 + lane];
+          for (int r = 0; r < 16; ++r)
+            acc[tm][r] += red[((((k2 - 1) * WN + wn) * MT + tm) * 16 + r) * 64 + lane];
+    }
   }
 
-  const float* bptr = bias + (size_t)e * N;
-  const int n = n0 + wn * 32 + lg * 4;
+  // ---- epilogue: bias (+ GELU, bf16), 32 rows at a time through LDS, then
+  //      written out as whole contiguous row segments (the accumulator layout
+  //      would otherwise scatter each store over 32 rows)
+  constexpr int ESZ = EPI == 0 ? 2 : 4;
+  constexpr int ROWB = S::OUT_ROW_BYTES(ESZ);
+  constexpr int CPR = S::BN * ESZ / 16;  // 16-byte chunks per output row
+  float4 bq[4];
+  {
+    const float* bptr = bias + (size_t)e * N + n0 + wn * 32 + lg * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bq[q] = *(const float4*)(bptr + q * 8);
+  }
+  char* tile = lds;
 #pragma unroll
   for (int tm = 0; tm < MT; ++tm) {
-    const int m = row0 + tm * 32 + li;
-    if (m < row_end) store_tile<EPI>(acc[tm], bptr, out, m, n, N);
+    if (row0 + tm * 32 >= row_end) break;  // uniform
+    __syncthreads();  // LDS free: previous pass copied out / reduction read
+    if (kw == 0) {
+      char* rowp = tile + li * ROWB + (wn * 32 + lg * 4) * ESZ;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float v0 = acc[tm][4 * q + 0] + bq[q].x, v1 = acc[tm][4 * q + 1] + bq[q].y;
+        const float v2 = acc[tm][4 * q + 2] + bq[q].z, v3 = acc[tm][4 * q + 3] + bq[q].w;
+        if (EPI == 0) {
+          uint2 pk;
+          pk.x = pack_bf16x2(gelu_tanh_bf16(v0), gelu_tanh_bf16(v1));
+          pk.y = pack_bf16x2(gelu_tanh_bf16(v2), gelu_tanh_bf16(v3));
+          *(uint2*)(rowp + q * 8 * ESZ) = pk;
+        } else {
+          *(float4*)(rowp + q * 8 * ESZ) = make_float4(v0, v1, v2, v3);
+        }
+      }
+    }
+    __syncthreads();
+    const int rows = min(32, row_end - (row0 + tm * 32));
+    char* gout = (char*)out + ((size_t)(row0 + tm * 32) * N + n0) * ESZ;
+    for (int i = tid; i < rows * CPR; i += 256) {
+      const int r = i / CPR, c = i - r * CPR;
+      *(u32x4*)(gout + (size_t)r * N * ESZ + c * 16) = *(const u32x4*)(tile + r * ROWB + c * 16);
+    }
   }
 }
 
@@ -512,27 +578,41 @@ int64_t grid_for(int64_t r_max, int BM, int E, int N, int BN) {
   return (g + NXCD - 1) / NXCD * NXCD;
 }
 
-template <int MT, int WN, int WK, int EPI, bool PK>
+template <int MT, int WN, int WK, int EPI, bool PK, int OCC>
 hipError_t launch_stream(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
                          const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
                          hipStream_t s) {
   const int64_t grid = grid_for(r_max, 32 * MT, E, N, 32 * WN);
-  hipLaunchKernelGGL((stream_gemm_kernel<MT, WN, WK, EPI, PK>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((stream_gemm_kernel<MT, WN, WK, EPI, PK, OCC>), dim3((unsigned)grid),
                      dim3(256), 0, s, A, W, bias, out, offsets, E, N, Kd);
   return hipGetLastError();
 }
 
+template <int MT, int WN, int WK, int EPI, bool PK>
+hipError_t launch_stream_occ(bool occ1, const uint16_t* A, const uint16_t* W, const float* bias,
+                             void* out, const int32_t* offsets, int E, int N, int Kd,
+                             int64_t r_max, hipStream_t s) {
+  // built only for the tall tiles, where one workgroup per CU is the common case
+  if constexpr (MT >= 4 && WN == 2)
+    if (occ1)
+      return launch_stream<MT, WN, WK, EPI, PK, 1>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+  return launch_stream<MT, WN, WK, EPI, PK, 2>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+}
+
 template <int MT, int EPI, bool PK>
-hipError_t launch_stream_mt(int wn, const uint16_t* A, const uint16_t* W, const float* bias,
-                            void* out, const int32_t* offsets, int E, int N, int Kd,
-                            int64_t r_max, hipStream_t s) {
+hipError_t launch_stream_mt(int wn, bool occ1, const uint16_t* A, const uint16_t* W,
+                            const float* bias, void* out, const int32_t* offsets, int E, int N,
+                            int Kd, int64_t r_max, hipStream_t s) {
   if (wn == 4)
-    return launch_stream<MT, 4, 1, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+    return launch_stream_occ<MT, 4, 1, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
+                                                s);
   // the 4-way k split keeps MT <= 3 (its reduction and ring outgrow the registers)
   if (wn == 2 || MT >= 4)
-    return launch_stream<MT, 2, 2, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+    return launch_stream_occ<MT, 2, 2, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
+                                                s);
   if constexpr (MT < 4)
-    return launch_stream<MT, 1, 4, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+    return launch_stream_occ<MT, 1, 4, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
+                                                s);
   return hipErrorInvalidValue;
 }
 
@@ -572,12 +652,17 @@ hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* b
   int wn = 1;
   if (N % 128 == 0 && mtiles * (N / 128) >= 256) wn = 4;
   else if (mtiles * (N / 64) >= 256 || mt >= 4) wn = 2;
+  // at most one workgroup of work per CU: build for occupancy 1 and prefetch deeper
+  const bool occ1 = mtiles * (N / (32 * wn)) <= 256;
   switch (mt) {
-    case 1: return launch_stream_mt<1, EPI, PK>(wn, A, W, bias, out, offsets, E, N, Kd, r_max, s);
-    case 2: return launch_stream_mt<2, EPI, PK>(wn, A, W, bias, out, offsets, E, N, Kd, r_max, s);
-    case 3: return launch_stream_mt<3, EPI, PK>(wn, A, W, bias, out, offsets, E, N, Kd, r_max, s);
-    case 4: return launch_stream_mt<4, EPI, PK>(wn, A, W, bias, out, offsets, E, N, Kd, r_max, s);
-    default: return launch_stream_mt<5, EPI, PK>(wn, A, W, bias, out, offsets, E, N, Kd, r_max, s);
+#define MOE_MT_CASE(M_)                                                                    \
+    return launch_stream_mt<M_, EPI, PK>(wn, occ1, A, W, bias, out, offsets, E, N, Kd, r_max, s)
+    case 1: MOE_MT_CASE(1);
+    case 2: MOE_MT_CASE(2);
+    case 3: MOE_MT_CASE(3);
+    case 4: MOE_MT_CASE(4);
+    default: MOE_MT_CASE(5);
+#undef MOE_MT_CASE
   }
 }
 
