@@ -5,16 +5,18 @@ combine, plus the ledger) on one MI355X, through the C ABI of libmoe.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--mode graph]
 
 A step is one pass of the whole path over one batch of tokens: moe_route,
-moe_dispatch, moe_expert_ffn and moe_combine on the main stream, and the
-ledger (moe_ledger_launch: its kernels plus the copy of its counters to a
-page-locked host stage) on a side stream that starts after the dispatch and
-joins before the step ends; the host decodes each step's ledger
-(moe_ledger_finalize) while the next step runs.  Inputs are resident in HBM.
+moe_dispatch, moe_expert_ffn, moe_combine and the ledger (moe_ledger_launch:
+its kernels plus the copy of its counters to a page-locked host stage), all
+on one stream (--ledger-stream side moves the ledger to a second stream that
+starts after the dispatch and joins before the step ends); the host decodes
+each step's ledger (moe_ledger_finalize) while the next step runs.  Inputs
+are resident in HBM.
 So that the 256 MB last-level cache cannot serve the weights, successive steps
 rotate over several copies of x and of all weights (>= 1 GiB in total).
 
-Modes: "graph" (default) captures each rotation's step once into a HIP graph
-and replays it; "eager" issues the pre-marshalled C calls every step.  Either
+Modes: "eager" (default) issues the pre-marshalled C calls every step;
+"graph" captures each rotation's step once into a HIP graph and replays it
+(measured slower than eager on this stack, so not the default).  Either
 way a second, eager timed pass records HIP events around each call on the
 stream it runs on; the expert-FFN interval (its two grouped-GEMM launches)
 gives the roofline of the dominant kernel.
@@ -47,12 +49,15 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2,
                    help="workload id (2 = the Switch-Base-shaped layer, the headline)")
-    p.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    p.add_argument("--mode", choices=["graph", "eager"], default="eager")
     p.add_argument("--weights", choices=["packed", "rowmajor"], default="packed",
                    help="expert weights in the packed fragment layout (packed once at setup, "
                         "as a server does at load time) or row-major")
     p.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
                    help="total bytes of rotated input copies (defeats the 256 MB cache)")
+    p.add_argument("--ledger-stream", choices=["side", "main"], default="main",
+                   help="run the ledger's kernels on a side stream beside the FFN, or after "
+                        "the combine on the main stream")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="rough budget of the CPU-oracle baseline")
@@ -139,7 +144,7 @@ def main():
     torch.cuda.synchronize()
 
     main_s = torch.cuda.Stream()
-    side_s = torch.cuda.Stream()
+    side_s = torch.cuda.Stream() if args.ledger_stream == "side" else None
     ledger_ws = torch.empty_like(bufs.ws)
     plans = [LayerPlan(bufs, *st, inp.src_rank, inp.owner_rank, wl.n_ep, 0.01, main=main_s,
                        side=side_s, ledger_ws=ledger_ws, packed=packed) for st in sets]
@@ -244,6 +249,7 @@ def main():
                                f"cf={wl.cf}", "T": wl.T, "h": wl.h, "E": wl.E, "K": wl.K,
                    "F": wl.F, "capacity_factor": wl.cf, "capacity": cap, "n_ep": wl.n_ep,
                    "mode": args.mode, "weights": "packed" if packed else "row-major",
+                   "ledger_stream": args.ledger_stream,
                    "rotated_copies": n_rot, "parallelism": "single GPU"},
         "routes_per_s": wl.A * K / elapsed,
         "accepted_routes_per_s": R * K / elapsed,

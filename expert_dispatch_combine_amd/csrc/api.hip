@@ -212,24 +212,42 @@ size_t moe_ledger_stage_bytes(const moe_cfg* cfg, int32_t n_ep) {
   return ledger_final_bytes(cfg->E, n_ep);
 }
 
+// Checks shared by moe_ledger_launch and moe_ledger.
+static int ledger_args(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_gate,
+                       const int32_t* route_row, const int32_t* src_rank,
+                       const int32_t* owner_rank, int32_t n_ep, void* ws, size_t ws_bytes) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!owner_rank || !ws) return MOE_ERR_INVALID_ARG;
+  if (n_ep < 1 || n_ep > kMaxRanks) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!topk_idx || !topk_gate || !route_row || !src_rank))
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe_workspace_bytes(cfg)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
 int moe_ledger_launch(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_gate,
                       const int32_t* route_row, const int32_t* src_rank,
                       const int32_t* owner_rank, int32_t n_ep, void* host_stage,
                       size_t stage_bytes, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_cfg(cfg);
+  int st = ledger_args(cfg, topk_idx, topk_gate, route_row, src_rank, owner_rank, n_ep, ws,
+                       ws_bytes);
   if (st != MOE_OK) return st;
-  if (!owner_rank || !ws || !host_stage) return MOE_ERR_INVALID_ARG;
-  if (n_ep < 1 || n_ep > kMaxRanks) return MOE_ERR_INVALID_ARG;
-  const int T = cfg->T, K = cfg->K, E = cfg->E;
-  if (T > 0 && (!topk_idx || !topk_gate || !route_row || !src_rank)) return MOE_ERR_INVALID_ARG;
-  if (ws_bytes < moe_workspace_bytes(cfg)) return MOE_ERR_SHAPE;
-  if (stage_bytes < ledger_final_bytes(E, n_ep)) return MOE_ERR_SHAPE;
+  if (!host_stage) return MOE_ERR_INVALID_ARG;
+  if (stage_bytes < ledger_final_bytes(cfg->E, n_ep)) return MOE_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
+  // page-locked host memory mapped into the device: the kernels write the
+  // stage themselves; otherwise the final area is copied into it
+  void* mapped = nullptr;
+  if (hipHostGetDevicePointer(&mapped, host_stage, 0) != hipSuccess) {
+    (void)hipGetLastError();  // not mapped: clear the sticky error, copy instead
+    mapped = nullptr;
+  }
   void* fin = nullptr;
   size_t fin_bytes = 0;
-  st = hip_status(launch_ledger(topk_idx, topk_gate, route_row, src_rank, owner_rank, T, K, E,
-                                n_ep, ws, &fin, &fin_bytes, s));
-  if (st != MOE_OK) return st;
+  st = hip_status(launch_ledger(topk_idx, topk_gate, route_row, src_rank, owner_rank, cfg->T,
+                                cfg->K, cfg->E, n_ep, ws, mapped, &fin, &fin_bytes, s));
+  if (st != MOE_OK || mapped) return st;
   if (hipMemcpyAsync(host_stage, fin, fin_bytes, hipMemcpyDeviceToHost, s) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
@@ -245,7 +263,7 @@ int moe_ledger_finalize(const moe_cfg* cfg, int64_t capacity, int32_t n_ep, doub
   const int T = cfg->T, K = cfg->K, E = cfg->E;
   const char* stage = (const char*)host_stage;
   const int64_t* h_load = (const int64_t*)stage;
-  const double* h_P = (const double*)(stage + (size_t)E * 8);
+  const uint64_t* h_P = (const uint64_t*)(stage + (size_t)E * 8);  // units of 2^-32
   const int64_t* h_cnt = (const int64_t*)(stage + (size_t)2 * E * 8);
   const int64_t* h_pair = (const int64_t*)(stage + (size_t)(2 * E + LC_N) * 8);
 
@@ -293,7 +311,7 @@ int moe_ledger_finalize(const moe_cfg* cfg, int64_t capacity, int32_t n_ep, doub
   double sfp = 0.0;
   for (int e = 0; e < E; ++e) {
     const double fe = T ? (double)h_load[e] / (double)T : 0.0;
-    const double pe = T ? h_P[e] / (double)T : 0.0;
+    const double pe = T ? (double)h_P[e] * 0x1p-32 / (double)T : 0.0;
     if (f) f[e] = fe;
     if (P) P[e] = pe;
     if (loads) loads[e] = h_load[e];
@@ -328,15 +346,20 @@ int moe_ledger(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_ga
                const int32_t* owner_rank, int32_t n_ep, double alpha, moe_ledger_t* out,
                int64_t* loads, double* f, double* P, int64_t* pair_routes, void* ws,
                size_t ws_bytes, void* stream) {
-  int st = check_cfg(cfg);
+  int st = ledger_args(cfg, topk_idx, topk_gate, route_row, src_rank, owner_rank, n_ep, ws,
+                       ws_bytes);
   if (st != MOE_OK) return st;
   if (!out || capacity < 0) return MOE_ERR_INVALID_ARG;
-  if (n_ep < 1 || n_ep > kMaxRanks) return MOE_ERR_INVALID_ARG;
-  std::vector<char> stage(ledger_final_bytes(cfg->E, n_ep));
-  st = moe_ledger_launch(cfg, topk_idx, topk_gate, route_row, src_rank, owner_rank, n_ep,
-                         stage.data(), stage.size(), ws, ws_bytes, stream);
+  hipStream_t s = (hipStream_t)stream;
+  void* fin = nullptr;
+  size_t fin_bytes = 0;
+  st = hip_status(launch_ledger(topk_idx, topk_gate, route_row, src_rank, owner_rank, cfg->T,
+                                cfg->K, cfg->E, n_ep, ws, nullptr, &fin, &fin_bytes, s));
   if (st != MOE_OK) return st;
-  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
+  std::vector<char> stage(fin_bytes);
+  if (hipMemcpyAsync(stage.data(), fin, fin_bytes, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
   return moe_ledger_finalize(cfg, capacity, n_ep, alpha, stage.data(), out, loads, f, P,
                              pair_routes);
 }

@@ -7,6 +7,8 @@
 //   out[t] = sum_{k ascending, route_row[t,k] >= 0} gate[t,k] * Y[route_row[t,k]]
 // in fp32, so each output element is written once by one thread in a fixed
 // order.  Each workgroup handles TB tokens; their rows/gates are staged in LDS.
+#include <type_traits>
+
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -15,7 +17,9 @@ namespace {
 
 constexpr int kMaxTB = 64;
 
-template <bool VEC>
+// Each thread takes U output vectors at a time and issues the U loads of one
+// k before their FMAs, so it waits on memory K times per U vectors.
+template <bool VEC, int U>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ route_row,
                                                       const float* __restrict__ gate,
@@ -23,6 +27,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int h, int TB) {
   __shared__ int s_row[kMaxTB * kMaxTopK];
   __shared__ float s_gate[kMaxTB * kMaxTopK];
+  using V = typename std::conditional<VEC, float4, float>::type;
+  constexpr int NV = VEC ? 4 : 1;
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * TB;
   const int ntok = min(TB, T - t0);
@@ -31,33 +37,46 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     s_gate[j] = gate[(size_t)t0 * K + j];
   }
   __syncthreads();
-  const int hv = VEC ? h / 4 : h;  // vectors per row
+  const int hv = h / NV;  // vectors per row
   const int total = ntok * hv;
-  for (int i = tid; i < total; i += 256) {
-    const int tl = i / hv, c = i - tl * hv;
-    const int* rows = s_row + tl * K;
-    const float* gs = s_gate + tl * K;
-    if (VEC) {
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int k = 0; k < K; ++k) {
-        const int r = rows[k];
-        if (r < 0) continue;
-        const float g = gs[k];
-        const float4 v = ((const float4*)(y + (size_t)r * h))[c];
-        acc.x = fmaf(g, v.x, acc.x);
-        acc.y = fmaf(g, v.y, acc.y);
-        acc.z = fmaf(g, v.z, acc.z);
-        acc.w = fmaf(g, v.w, acc.w);
+  const V* yv = (const V*)y;
+  V* ov = (V*)(out + (size_t)t0 * h);
+  for (int i0 = tid; i0 < total; i0 += 256 * U) {
+    int tl[U], c[U];
+    float acc[U][NV];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = min(i0 + u * 256, total - 1);
+      tl[u] = i / hv;
+      c[u] = i - tl[u] * hv;
+#pragma unroll
+      for (int q = 0; q < NV; ++q) acc[u][q] = 0.f;
+    }
+    for (int k = 0; k < K; ++k) {
+      V v[U];
+      int r[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        r[u] = s_row[tl[u] * K + k];
+        if (r[u] >= 0) v[u] = yv[(size_t)r[u] * hv + c[u]];
       }
-      ((float4*)(out + (size_t)(t0 + tl) * h))[c] = acc;
-    } else {
-      float acc = 0.f;
-      for (int k = 0; k < K; ++k) {
-        const int r = rows[k];
-        if (r < 0) continue;
-        acc = fmaf(gs[k], y[(size_t)r * h + c], acc);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (r[u] < 0) continue;
+        const float g = s_gate[tl[u] * K + k];
+        const float* vf = (const float*)&v[u];
+#pragma unroll
+        for (int q = 0; q < NV; ++q) acc[u][q] = fmaf(g, vf[q], acc[u][q]);
       }
-      out[(size_t)(t0 + tl) * h + c] = acc;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u * 256 >= total) continue;
+      V o;
+      float* of = (float*)&o;
+#pragma unroll
+      for (int q = 0; q < NV; ++q) of[q] = acc[u][q];
+      ov[(size_t)tl[u] * hv + c[u]] = o;
     }
   }
 }
@@ -67,17 +86,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_combine(const float* y, const int32_t* route_row, const float* gate,
                           float* out, int T, int K, int h, hipStream_t s) {
   if (T == 0 || h == 0) return hipSuccess;
+  constexpr int U = 4;
   const bool vec = (h % 4) == 0;
   const int hv = vec ? h / 4 : h;
-  int TB = (1024 + hv - 1) / hv;  // about 4 vectors per thread
+  int TB = 256 * U / hv;  // about U vectors per thread
   if (TB > kMaxTB) TB = kMaxTB;
   if (TB < 1) TB = 1;
   const int grid = (T + TB - 1) / TB;
   if (vec)
-    hipLaunchKernelGGL((combine_kernel<true>), dim3(grid), dim3(256), 0, s, y, route_row, gate,
-                       out, T, K, h, TB);
+    hipLaunchKernelGGL((combine_kernel<true, U>), dim3(grid), dim3(256), 0, s, y, route_row,
+                       gate, out, T, K, h, TB);
   else
-    hipLaunchKernelGGL((combine_kernel<false>), dim3(grid), dim3(256), 0, s, y, route_row,
+    hipLaunchKernelGGL((combine_kernel<false, U>), dim3(grid), dim3(256), 0, s, y, route_row,
                        gate, out, T, K, h, TB);
   return hipGetLastError();
 }

@@ -14,6 +14,9 @@
 //   slot kernel   : prefix over earlier blocks + in-block wave multisplit
 //                   (ballots on the id bits) -> rank, row, row_token, offsets
 //   gather kernel : x_disp[row] = x[row_token[row]] with 16-byte vectors
+// Up to kSmallDispatchRoutes routes (16-byte-vector rows) all three run as one
+// launch: every block histograms all A routes itself (the expert totals and
+// the counts before its own 32 routes), so no block waits on another.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -62,6 +65,32 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh_wave, int tid
   return prefix + incl - v;
 }
 
+// Exclusive scan over experts of min(tot[e], cap) into off[0..E] (off[E] =
+// R); E <= kMaxExperts = 4 * 256.
+__device__ __forceinline__ void accepted_offsets(const int* tot, int* off, int E, int64_t cap,
+                                                 int* sh_wave, int tid) {
+  const int per_thread = (E + 255) / 256;
+  int accv[4];
+  int my_acc = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid * per_thread + j;
+    accv[j] = (j < per_thread && e < E) ? (int)min((int64_t)tot[e], cap) : 0;
+    my_acc += accv[j];
+  }
+  int excl = block_exclusive_scan(my_acc, sh_wave, tid);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid * per_thread + j;
+    if (j < per_thread && e < E) {
+      off[e] = excl;
+      excl += accv[j];
+    }
+  }
+  if (tid == 255) off[E] = excl;
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(256) void slot_kernel(
     const int32_t* __restrict__ idx, int64_t A, int K, int E, int64_t cap, int nblocks,
     const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -100,30 +129,11 @@ __global__ __launch_bounds__(256) void slot_kernel(
       bef += pbef[sl * E + e];
     }
     run[e] = bef;
-    off[e] = (int)min((int64_t)tot, cap);  // accepted count, scanned in place below
+    ptot[e] = tot;  // each e is read and written by this thread only
     if (b == 0 && load_out) load_out[e] = tot;
   }
   __syncthreads();
-  const int per_thread = (E + 255) / 256;  // consecutive experts per thread (<= 4)
-  int accv[4];
-  int my_acc = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = tid * per_thread + j;
-    accv[j] = (j < per_thread && e < E) ? off[e] : 0;
-    my_acc += accv[j];
-  }
-  int excl = block_exclusive_scan(my_acc, sh_wave, tid);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = tid * per_thread + j;
-    if (j < per_thread && e < E) {
-      off[e] = excl;
-      excl += accv[j];
-    }
-  }
-  if (tid == 255) off[E] = excl;  // the last thread ends at the grand total
-  __syncthreads();
+  accepted_offsets(ptot, off, E, cap, sh_wave, tid);
   if (b == 0)
     for (int e = tid; e <= E; e += 256) offsets[e] = off[e];
 
@@ -170,32 +180,137 @@ __global__ __launch_bounds__(256) void slot_kernel(
   }
 }
 
+// Copy NR token rows: xd[dst[r]] = x[src[r]] for r < NR with dst[r] >= 0
+// (row indices, in LDS).  The NR * row_vecs 16-byte vectors are spread over
+// the 256 threads; each thread issues U loads before their stores.
+template <int NR, int U>
+__device__ __forceinline__ void copy_rows(const u32x4* __restrict__ x, u32x4* __restrict__ xd,
+                                          const int* dst, const int* src, int row_vecs) {
+  const int nv = NR * row_vecs;
+  for (int j0 = threadIdx.x; j0 < nv; j0 += 256 * U) {
+    u32x4 v[U];
+    int64_t to[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * 256;
+      const int r = j / row_vecs;
+      const int c = j - r * row_vecs;
+      to[u] = -1;
+      if (j < nv && dst[r] >= 0) {
+        v[u] = x[(int64_t)src[r] * row_vecs + c];
+        to[u] = (int64_t)dst[r] * row_vecs + c;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (to[u] >= 0) xd[to[u]] = v[u];
+  }
+}
+
 // x_disp[row] = x[row_token[row]] for row < R = offsets[E]; rows are
 // row_vecs 16-byte vectors long.  Each workgroup moves ROWS rows.
-// All ROWS loads of a column are issued before the stores, so each thread
-// keeps ROWS 16-byte reads in flight.
 template <int ROWS>
 __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x,
                                                      const int32_t* __restrict__ row_token,
                                                      const int32_t* __restrict__ offsets,
                                                      int E, int row_vecs,
                                                      u32x4* __restrict__ xd) {
+  __shared__ int dst[ROWS], src[ROWS];
   const int R = offsets[E];
   const int r0 = blockIdx.x * ROWS;
   if (r0 >= R) return;
-  int64_t src[ROWS];
-#pragma unroll
-  for (int r = 0; r < ROWS; ++r)
-    src[r] = (r0 + r < R) ? (int64_t)row_token[r0 + r] * row_vecs : -1;
-  for (int c = threadIdx.x; c < row_vecs; c += 256) {
-    u32x4 v[ROWS];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r)
-      if (src[r] >= 0) v[r] = x[src[r] + c];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r)
-      if (src[r] >= 0) xd[(int64_t)(r0 + r) * row_vecs + c] = v[r];
+  if (threadIdx.x < ROWS) {
+    const int r = r0 + threadIdx.x;
+    dst[threadIdx.x] = r < R ? r : -1;
+    src[threadIdx.x] = r < R ? row_token[r] : 0;
   }
+  __syncthreads();
+  copy_rows<ROWS, 8>(x, xd, dst, src, row_vecs);
+}
+
+// The whole dispatch for A <= kSmallDispatchRoutes in one launch; block b
+// owns routes [32b, 32b + 32).
+constexpr int SBR = 32;
+__global__ __launch_bounds__(256) void dispatch_small_kernel(
+    const int32_t* __restrict__ idx, int A, int K, int E, int64_t cap,
+    const u32x4* __restrict__ x, int row_vecs, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ route_rank, int32_t* __restrict__ route_row,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ load_out, u32x4* __restrict__ xd) {
+  __shared__ int tot[kMaxExperts], bef[kMaxExperts], off[kMaxExperts + 1];
+  __shared__ int sh_wave[4];
+  __shared__ int dst[SBR], src[SBR];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int base = blockIdx.x * SBR;
+  for (int e = tid; e < E; e += 256) tot[e] = bef[e] = 0;
+  __syncthreads();
+  // all routes: totals, and the routes before this block (the stable order).
+  // Eight loads per thread in flight; lanes of a wave with the same expert
+  // are found with ballots on the id bits, and one of them adds their count.
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int i0 = 0; i0 < A; i0 += 256 * 8) {
+    int ids[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + tid;
+      ids[u] = i < A ? idx[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + tid;
+      const int id = ids[u];
+      const bool valid = id >= 0 && id < E;
+      uint64_t m = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool on = valid && ((id >> bit) & 1);
+        const uint64_t bm = __ballot(on);
+        m &= on ? bm : ~bm;
+      }
+      const uint64_t before = __ballot(i < base);
+      if (valid && (m & lt_mask) == 0) {
+        atomicAdd(&tot[id], __popcll(m));
+        const int nb = __popcll(m & before);
+        if (nb) atomicAdd(&bef[id], nb);
+      }
+    }
+  }
+  __syncthreads();
+  accepted_offsets(tot, off, E, cap, sh_wave, tid);
+  if (blockIdx.x == 0) {
+    for (int e = tid; e <= E; e += 256) offsets[e] = off[e];
+    if (load_out)
+      for (int e = tid; e < E; e += 256) load_out[e] = tot[e];
+  }
+  if (wave == 0) {
+    // rank = routes before the block + lanes below with the same expert
+    const int i = base + lane;
+    int id = -1;
+    if (lane < SBR && i < A) id = idx[i];
+    const bool valid = lane < SBR && i < A && id >= 0 && id < E;
+    uint64_t m = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = valid && ((id >> bit) & 1);
+      const uint64_t bm = __ballot(on);
+      m &= on ? bm : ~bm;
+    }
+    const int rank = valid ? bef[id] + __popcll(m & lt_mask) : -1;
+    int row = -1;
+    if (valid && (int64_t)rank < cap) {
+      row = off[id] + rank;
+      row_token[row] = i / K;
+    }
+    if (lane < SBR && i < A) {
+      route_rank[i] = rank;
+      route_row[i] = row;
+    }
+    if (lane < SBR) {
+      dst[lane] = row;
+      src[lane] = i / K;
+    }
+  }
+  __syncthreads();
+  copy_rows<SBR, 4>(x, xd, dst, src, row_vecs);
 }
 
 // the same gather for rows that are not a whole number of 16-byte vectors
@@ -224,6 +339,15 @@ hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int64_t A, in
                            int32_t* offsets, int32_t* route_rank, int32_t* route_row,
                            int32_t* row_token, void* x_disp, int32_t* load, void* ws,
                            hipStream_t s) {
+  const bool vec = row_bytes % 16 == 0 && ((uintptr_t)x & 15u) == 0 &&
+                   ((uintptr_t)x_disp & 15u) == 0;
+  if (A > 0 && A <= kSmallDispatchRoutes && r_max > 0 && vec) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3((unsigned)((A + SBR - 1) / SBR)), dim3(256),
+                       0, s, topk_idx, (int)A, K, E, cap, (const u32x4*)x,
+                       (int)(row_bytes / 16), offsets, route_rank, route_row, row_token, load,
+                       (u32x4*)x_disp);
+    return hipGetLastError();
+  }
   const int nb = (int)((A + RPB - 1) / RPB);
   int32_t* counts = (int32_t*)ws;
   if (nb > 0) {
@@ -236,8 +360,8 @@ hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int64_t A, in
                      cap, nb, counts, offsets, route_rank, route_row, row_token, load);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || r_max == 0) return err;
-  if (row_bytes % 16 == 0 && ((uintptr_t)x & 15u) == 0 && ((uintptr_t)x_disp & 15u) == 0) {
-    constexpr int ROWS = 8;
+  if (vec) {
+    constexpr int ROWS = 16;
     const int64_t grid = (r_max + ROWS - 1) / ROWS;
     hipLaunchKernelGGL((gather_kernel<ROWS>), dim3((unsigned)grid), dim3(256), 0, s,
                        (const u32x4*)x, row_token, offsets, E, (int)(row_bytes / 16),

@@ -9,11 +9,18 @@
 // "MoE大模型专家并行与动态路由优化" 2.2 (round-robin owner e % N) and 3.2
 // (f_i, P_i, L_aux).
 //
-// Device part: one workgroup per 2048 routes builds integer histograms in LDS
-// and per-expert gate sums in float64 with a fixed summation order; a second
-// kernel adds the per-block partials in block order.  Integer counters are
-// exact, and the float64 sums are deterministic run to run.  The host
-// finishes the few scalar formulas in float64.
+// Every counter is an integer, so the result does not depend on the order in
+// which routes are added.  The gate sums are integers too: each fp32 gate
+// (in [0, 1]) is rounded to a multiple of 2^-32 and the multiples are added
+// exactly in 64 bits (the sum of at most 2^31 gates stays below 2^63); the
+// host divides by 2^32.  Each route adds at most 2^-33 of rounding error.
+//
+// Device part: one workgroup per 512 routes builds LDS histograms and a
+// second kernel adds the per-block partials (one wave per output value).  Up
+// to kSmallLedgerRoutes routes one workgroup takes them all and writes the
+// final area itself.  The final area may be page-locked host memory (its
+// device address), which spares a copy.  The host finishes the few scalar
+// formulas in float64.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -21,11 +28,10 @@ namespace moe {
 namespace {
 
 constexpr int RPBL = kLedgerRoutesPerBlock;
-constexpr int PER_THREAD = RPBL / 256;
 
 struct LedgerWs {
   int32_t* blk_load;   // [nb][E]
-  double* blk_P;       // [nb][E]
+  uint64_t* blk_P;     // [nb][E] gate sums, units of 2^-32
   int64_t* blk_cnt;    // [nb][LC_N]
   int32_t* blk_pair;   // [nb][n_ep*n_ep]
   char* fin;           // final area
@@ -40,71 +46,112 @@ LedgerWs carve(void* ws, int64_t A, int E, int n_ep) {
   size_t o = 0;
   w.blk_load = (int32_t*)(p + o);
   o = align_up(o + (size_t)nb * E * sizeof(int32_t), 256);
-  w.blk_P = (double*)(p + o);
-  o = align_up(o + (size_t)nb * E * sizeof(double), 256);
+  w.blk_P = (uint64_t*)(p + o);
+  o = align_up(o + (size_t)nb * E * sizeof(uint64_t), 256);
   w.blk_cnt = (int64_t*)(p + o);
   o = align_up(o + (size_t)nb * LC_N * sizeof(int64_t), 256);
   w.blk_pair = (int32_t*)(p + o);
   o = align_up(o + (size_t)nb * n_ep * n_ep * sizeof(int32_t), 256);
   w.fin = p + o;
-  w.fin_bytes = (size_t)(2 * E + LC_N + n_ep * n_ep) * 8;
+  w.fin_bytes = ledger_final_bytes(E, n_ep);
   o = align_up(o + w.fin_bytes, 256);
   w.total = o;
   return w;
 }
 
+// Final area layout (8 bytes each): loads[E] int64, P[E] uint64 (units of
+// 2^-32), counters[LC_N] int64, pair[n_ep * n_ep] int64.
+struct FinalArea {
+  int64_t* load;
+  uint64_t* P;
+  int64_t* cnt;
+  int64_t* pair;
+};
+
+__device__ __forceinline__ FinalArea final_area(char* fin, int E) {
+  return {(int64_t*)fin, (uint64_t*)(fin + (size_t)E * 8), (int64_t*)(fin + (size_t)2 * E * 8),
+          (int64_t*)(fin + (size_t)(2 * E + LC_N) * 8)};
+}
+
+// gate (in [0, 1]) -> nearest multiple of 2^-32, as an integer
+__device__ __forceinline__ unsigned long long gate_fixed(float g) {
+  return __double2ull_rn((double)g * 4294967296.0);
+}
+
+// RPB routes per workgroup.  FINAL (a one-workgroup launch): write the final
+// area `fin` directly instead of the per-block partials.
+template <int RPB, bool FINAL>
 __global__ __launch_bounds__(256) void ledger_partial_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ gate,
     const int32_t* __restrict__ route_row, const int32_t* __restrict__ src,
     const int32_t* __restrict__ owner, int64_t A, int K, int E, int n_ep,
-    int32_t* __restrict__ blk_load, double* __restrict__ blk_P, int64_t* __restrict__ blk_cnt,
-    int32_t* __restrict__ blk_pair) {
+    int32_t* __restrict__ blk_load, uint64_t* __restrict__ blk_P,
+    int64_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_pair, char* __restrict__ fin) {
+  constexpr int PER_THREAD = RPB / 256;
   __shared__ int s_load[kMaxExperts];
+  __shared__ unsigned long long s_P[kMaxExperts];
+  __shared__ int s_owner[kMaxExperts];
   __shared__ int s_pair[kMaxRanks * kMaxRanks];
-  __shared__ int s_idx[RPBL];
-  __shared__ float s_gate[RPBL];
-  __shared__ double s_part[kMaxExperts];
   __shared__ int s_cnt[LC_N];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int np = n_ep * n_ep;
-  for (int e = tid; e < E; e += 256) s_load[e] = 0;
+  for (int e = tid; e < E; e += 256) {
+    s_load[e] = 0;
+    s_P[e] = 0ull;
+    s_owner[e] = owner[e];
+  }
   for (int j = tid; j < np; j += 256) s_pair[j] = 0;
   if (tid < LC_N) s_cnt[tid] = 0;
-  __syncthreads();
 
-  const int64_t base = (int64_t)b * RPBL;
-  const int n = (int)min((int64_t)RPBL, A - base);
+  const int64_t base = (int64_t)b * RPB;
+  const int n = (int)min((int64_t)RPB, A - base);
   int c_lall = 0, c_call = 0, c_lacc = 0, c_cacc = 0, c_acc = 0, c_bad_id = 0, c_bad_rank = 0;
+  // batches of U routes per thread; every global load of a batch is issued
+  // before any of them is used.  The first batch's loads overlap the LDS
+  // initialisation above; the barrier that publishes it follows them.
+  constexpr int U = PER_THREAD < 8 ? PER_THREAD : 8;
+  for (int u0 = 0; u0 < PER_THREAD; u0 += U) {
+    if (u0 > 0 && u0 * 256 >= n) break;  // block-uniform
+    int ids[U], rows[U], srcs[U];
+    float gs[U];
 #pragma unroll
-  for (int u = 0; u < PER_THREAD; ++u) {
-    const int j = u * 256 + tid;
-    if (j >= n) continue;
-    const int64_t i = base + j;
-    const int id = idx[i];
-    const bool valid = id >= 0 && id < E;
-    s_idx[j] = valid ? id : -1;
-    s_gate[j] = gate[i];
-    if (!valid) {
-      ++c_bad_id;
-      continue;
+    for (int u = 0; u < U; ++u) {
+      const int j = (u0 + u) * 256 + tid;
+      const int64_t i = base + (j < n ? j : 0);
+      ids[u] = idx[i];
+      gs[u] = gate[i];
+      rows[u] = route_row[i];
+      srcs[u] = src[i / K];
     }
-    atomicAdd(&s_load[id], 1);
-    const int row = route_row[i];
-    if (row >= 0) ++c_acc;
-    const int sr = src[i / K];
-    const int orank = owner[id];
-    if (sr < 0 || sr >= n_ep || orank < 0 || orank >= n_ep) {
-      ++c_bad_rank;
-      continue;
-    }
-    const bool local = sr == orank;
-    c_lall += local;
-    c_call += !local;
-    if (row >= 0) {
-      c_lacc += local;
-      c_cacc += !local;
-      atomicAdd(&s_pair[sr * n_ep + orank], 1);
+    if (u0 == 0) __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = (u0 + u) * 256 + tid;
+      if (j >= n) continue;
+      const int id = ids[u];
+      if (id < 0 || id >= E) {
+        ++c_bad_id;
+        continue;
+      }
+      atomicAdd(&s_load[id], 1);
+      atomicAdd(&s_P[id], gate_fixed(gs[u]));
+      const int row = rows[u];
+      if (row >= 0) ++c_acc;
+      const int sr = srcs[u];
+      const int orank = s_owner[id];
+      if (sr < 0 || sr >= n_ep || orank < 0 || orank >= n_ep) {
+        ++c_bad_rank;
+        continue;
+      }
+      const bool local = sr == orank;
+      c_lall += local;
+      c_call += !local;
+      if (row >= 0) {
+        c_lacc += local;
+        c_cacc += !local;
+        atomicAdd(&s_pair[sr * n_ep + orank], 1);
+      }
     }
   }
   // wave sums of the scalar counters, then one LDS atomic per wave
@@ -127,58 +174,58 @@ __global__ __launch_bounds__(256) void ledger_partial_kernel(
   }
   __syncthreads();
 
-  // per-expert gate sums, fixed order: S threads per expert, thread `sl`
-  // takes routes sl, sl+S, ...; the S partials are then added in sl order
-  const int S = (E >= 256) ? 1 : (256 / E);
-  for (int w = tid; w < E * S; w += 256) {
-    const int e = w % E, sl = w / E;
-    double sum = 0.0;
-    for (int j = sl; j < n; j += S)
-      if (s_idx[j] == e) sum += (double)s_gate[j];
-    s_part[w] = sum;
+  if (FINAL) {
+    const FinalArea f = final_area(fin, E);
+    for (int e = tid; e < E; e += 256) {
+      f.P[e] = s_P[e];
+      f.load[e] = s_load[e];
+    }
+    for (int j = tid; j < np; j += 256) f.pair[j] = s_pair[j];
+    if (tid < LC_N) f.cnt[tid] = s_cnt[tid];
+    return;
   }
-  __syncthreads();
   for (int e = tid; e < E; e += 256) {
-    double sum = 0.0;
-    for (int sl = 0; sl < S; ++sl) sum += s_part[sl * E + e];
-    blk_P[(size_t)b * E + e] = sum;
+    blk_P[(size_t)b * E + e] = s_P[e];
     blk_load[(size_t)b * E + e] = s_load[e];
   }
   for (int j = tid; j < np; j += 256) blk_pair[(size_t)b * np + j] = s_pair[j];
   if (tid < LC_N) blk_cnt[(size_t)b * LC_N + tid] = s_cnt[tid];
 }
 
-// final[q] = sum over blocks (in block order) of the per-block partial q
+// final[q] = sum over blocks of the per-block partial q; one wave per q, its
+// lanes take blocks lane, lane + 64, ... (integers: any order is exact)
 __global__ __launch_bounds__(256) void ledger_reduce_kernel(
     int nb, int E, int n_ep, const int32_t* __restrict__ blk_load,
-    const double* __restrict__ blk_P, const int64_t* __restrict__ blk_cnt,
+    const uint64_t* __restrict__ blk_P, const int64_t* __restrict__ blk_cnt,
     const int32_t* __restrict__ blk_pair, char* __restrict__ fin) {
   const int np = n_ep * n_ep;
-  const int q = blockIdx.x * 256 + threadIdx.x;
-  int64_t* f_load = (int64_t*)fin;
-  double* f_P = (double*)(fin + (size_t)E * 8);
-  int64_t* f_cnt = (int64_t*)(fin + (size_t)2 * E * 8);
-  int64_t* f_pair = (int64_t*)(fin + (size_t)(2 * E + LC_N) * 8);
+  const int lane = threadIdx.x & 63;
+  const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int items = 2 * E + LC_N + np;
+  if (q >= items) return;  // whole waves leave together
+  const FinalArea fa = final_area(fin, E);
+  uint64_t s = 0;  // two's complement: signed partials add up the same way
   if (q < E) {
-    int64_t s = 0;
-    for (int b = 0; b < nb; ++b) s += blk_load[(size_t)b * E + q];
-    f_load[q] = s;
+    for (int b = lane; b < nb; b += 64) s += (uint64_t)(int64_t)blk_load[(size_t)b * E + q];
   } else if (q < 2 * E) {
-    const int e = q - E;
-    double s = 0.0;
-    for (int b = 0; b < nb; ++b) s += blk_P[(size_t)b * E + e];
-    f_P[e] = s;
+    for (int b = lane; b < nb; b += 64) s += blk_P[(size_t)b * E + (q - E)];
   } else if (q < 2 * E + LC_N) {
-    const int c = q - 2 * E;
-    int64_t s = 0;
-    for (int b = 0; b < nb; ++b) s += blk_cnt[(size_t)b * LC_N + c];
-    f_cnt[c] = s;
-  } else if (q < 2 * E + LC_N + np) {
+    for (int b = lane; b < nb; b += 64) s += (uint64_t)blk_cnt[(size_t)b * LC_N + (q - 2 * E)];
+  } else {
     const int j = q - 2 * E - LC_N;
-    int64_t s = 0;
-    for (int b = 0; b < nb; ++b) s += blk_pair[(size_t)b * np + j];
-    f_pair[j] = s;
+    for (int b = lane; b < nb; b += 64) s += (uint64_t)(int64_t)blk_pair[(size_t)b * np + j];
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)s, off, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(s >> 32), off, 64);
+    s += ((uint64_t)hi << 32) | lo;
+  }
+  if (lane != 0) return;
+  if (q < E) fa.load[q] = (int64_t)s;
+  else if (q < 2 * E) fa.P[q - E] = s;
+  else if (q < 2 * E + LC_N) fa.cnt[q - 2 * E] = (int64_t)s;
+  else fa.pair[q - 2 * E - LC_N] = (int64_t)s;
 }
 
 }  // namespace
@@ -187,22 +234,30 @@ size_t ledger_ws_bytes(int64_t A, int E, int n_ep) { return carve(nullptr, A, E,
 
 hipError_t launch_ledger(const int32_t* idx, const float* gate, const int32_t* route_row,
                          const int32_t* src, const int32_t* owner, int T, int K, int E,
-                         int n_ep, void* ws, void** final_area, size_t* final_bytes,
-                         hipStream_t s) {
+                         int n_ep, void* ws, void* fin_dst, void** final_area_out,
+                         size_t* final_bytes, hipStream_t s) {
   const int64_t A = (int64_t)T * K;
   LedgerWs w = carve(ws, A, E, n_ep);
+  char* fin = fin_dst ? (char*)fin_dst : w.fin;
+  *final_area_out = fin;
+  *final_bytes = w.fin_bytes;
+  if (A > 0 && A <= kSmallLedgerRoutes) {
+    hipLaunchKernelGGL((ledger_partial_kernel<kSmallLedgerRoutes, true>), dim3(1), dim3(256), 0,
+                       s, idx, gate, route_row, src, owner, A, K, E, n_ep, nullptr, nullptr,
+                       nullptr, nullptr, fin);
+    return hipGetLastError();
+  }
   const int nb = A > 0 ? (int)((A + RPBL - 1) / RPBL) : 0;
   if (nb > 0) {
-    hipLaunchKernelGGL(ledger_partial_kernel, dim3(nb), dim3(256), 0, s, idx, gate, route_row,
-                       src, owner, A, K, E, n_ep, w.blk_load, w.blk_P, w.blk_cnt, w.blk_pair);
+    hipLaunchKernelGGL((ledger_partial_kernel<RPBL, false>), dim3(nb), dim3(256), 0, s, idx,
+                       gate, route_row, src, owner, A, K, E, n_ep, w.blk_load, w.blk_P,
+                       w.blk_cnt, w.blk_pair, nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   const int items = 2 * E + LC_N + n_ep * n_ep;
-  hipLaunchKernelGGL(ledger_reduce_kernel, dim3((items + 255) / 256), dim3(256), 0, s, nb, E,
-                     n_ep, w.blk_load, w.blk_P, w.blk_cnt, w.blk_pair, w.fin);
-  *final_area = w.fin;
-  *final_bytes = w.fin_bytes;
+  hipLaunchKernelGGL(ledger_reduce_kernel, dim3((items + 3) / 4), dim3(256), 0, s, nb, E, n_ep,
+                     w.blk_load, w.blk_P, w.blk_cnt, w.blk_pair, fin);
   return hipGetLastError();
 }
 

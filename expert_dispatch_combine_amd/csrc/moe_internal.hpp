@@ -16,8 +16,12 @@ constexpr int kMaxRanks = 64;
 
 // Routes handled by one workgroup of the dispatch count / slot kernels.
 constexpr int kDispatchRoutesPerBlock = 1024;
+// routes up to which the whole dispatch runs as one launch
+constexpr int kSmallDispatchRoutes = 8192;
 // Routes handled by one workgroup of the ledger partial kernel.
 constexpr int kLedgerRoutesPerBlock = 512;
+// routes up to which one workgroup computes the whole ledger
+constexpr int kSmallLedgerRoutes = 4096;
 // Scalar counters of the ledger, per block and in the final area.
 enum LedgerCounter {
   LC_LOCAL_ALL = 0,
@@ -97,9 +101,11 @@ hipError_t launch_combine(const float* y, const int32_t* route_row, const float*
 // Ledger: per-block partials then a fixed-order reduction into `final_area`
 // (layout: loads[E] int64 | P[E] double | counters[LC_N] int64 |
 //  pairs[n_ep*n_ep] int64).
+// fin_dst: device-accessible destination of the final area (e.g. the device
+// address of page-locked host memory), or NULL for the area in `ws`.
 hipError_t launch_ledger(const int32_t* idx, const float* gate, const int32_t* route_row,
                          const int32_t* src, const int32_t* owner, int T, int K, int E,
-                         int n_ep, void* ws, void** final_area, size_t* final_bytes,
-                         hipStream_t s);
+                         int n_ep, void* ws, void* fin_dst, void** final_area,
+                         size_t* final_bytes, hipStream_t s);
 
 }  // namespace moe

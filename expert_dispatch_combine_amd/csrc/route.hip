@@ -157,40 +157,29 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // wave w takes k-steps w, w+4, ...; each trip issues the loads of U steps
+  // before their MFMAs, so a wave waits on memory once per U steps
+  constexpr int U = NT == 4 ? 4 : 8;
   const int nsteps = h / 32;
-  int s = wave;
-  // two steps per trip keep two sets of loads in flight
-  for (; s + 4 < nsteps; s += 8) {
-    const int k0 = s * 32, k1 = (s + 4) * 32;
-    const uint4 xb0 = *(const uint4*)(xrow + k0);
-    const uint4 xb1 = *(const uint4*)(xrow + k1);
-    uint4 wa0[NT], wa1[NT];
+  for (int s0 = wave; s0 < nsteps; s0 += 4 * U) {
+    uint4 xb[U], wa[U][NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      wa0[nt] = *(const uint4*)(wrow[nt] + k0);
-      wa1[nt] = *(const uint4*)(wrow[nt] + k1);
+    for (int u = 0; u < U; ++u) {
+      const int k = (s0 + 4 * u) * 32;
+      if (s0 + 4 * u < nsteps) {
+        xb[u] = *(const uint4*)(xrow + k);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) wa[u][nt] = *(const uint4*)(wrow[nt] + k);
+      }
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa0[nt]),
-                                                        __builtin_bit_cast(bf16x8, xb0),
-                                                        acc[nt], 0, 0, 0);
+    for (int u = 0; u < U; ++u)
+      if (s0 + 4 * u < nsteps)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa1[nt]),
-                                                        __builtin_bit_cast(bf16x8, xb1),
-                                                        acc[nt], 0, 0, 0);
-  }
-  for (; s < nsteps; s += 4) {
-    const int k0 = s * 32;
-    const uint4 xb0 = *(const uint4*)(xrow + k0);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint4 wa = *(const uint4*)(wrow[nt] + k0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa),
-                                                        __builtin_bit_cast(bf16x8, xb0),
-                                                        acc[nt], 0, 0, 0);
-    }
+        for (int nt = 0; nt < NT; ++nt)
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa[u][nt]),
+                                                            __builtin_bit_cast(bf16x8, xb[u]),
+                                                            acc[nt], 0, 0, 0);
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)

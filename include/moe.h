@@ -213,10 +213,13 @@ int moe_ledger(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_ga
 
 /* The same ledger in two halves, so that a serving loop (or a captured HIP
  * graph) never waits on the host:
- *   moe_ledger_launch  enqueues the counting kernels and an asynchronous copy
- *                      of the compact counters into `host_stage` (caller's
- *                      host memory of moe_ledger_stage_bytes(cfg, n_ep) bytes;
- *                      page-locked memory keeps the copy asynchronous);
+ *   moe_ledger_launch  enqueues the counting kernels, whose compact counters
+ *                      end up in `host_stage` (caller's host memory of
+ *                      moe_ledger_stage_bytes(cfg, n_ep) bytes).  Page-locked
+ *                      memory mapped into the device address space (what
+ *                      hipHostMalloc returns) is written by the kernels
+ *                      themselves; any other host memory receives an
+ *                      asynchronous copy enqueued after them;
  *   moe_ledger_finalize, once that copy has completed (stream or event
  *                      synchronisation by the caller), turns the stage into
  *                      the same outputs as moe_ledger.  Pure host function.
