@@ -77,6 +77,30 @@ def algorithmic(wl, R, E_nz):
     }
 
 
+def committed_traffic(kernel, workload):
+    """HBM bytes per call of `kernel` on `workload` from the rocprofv3 counter
+    summary committed under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled
+    by a plain copy's reading), or None when there is none or the kernel's
+    sources have changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path, encoding="utf-8") as fh:
+            for line in fh:
+                if not line.startswith("traffic-json: "):
+                    continue
+                rec = json.loads(line[len("traffic-json: "):])
+                if rec.get("kernel") != kernel or rec.get("workload") != workload:
+                    continue
+                h = hashlib.sha256()
+                for src in rec["sources"]:
+                    with open(os.path.join(ROOT, src), "rb") as sf:
+                        h.update(sf.read())
+                if h.hexdigest() == rec["sources_sha256"]:
+                    return int(rec["bytes_per_call"])
+    return None
+
+
 def cpu_baseline(wl, inp, budget_s):
     """The oracle as it stands, on the host cores: the whole layer of the same
     workload (route -> dispatch -> FFN -> combine, float64), timed per pass."""
@@ -223,7 +247,7 @@ def main():
         roof = {"bound": "mfma", "achieved": alg["ffn_flops"] / ffn_s / 1e12,
                 "peak": peak_flops, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = committed_traffic("expert_ffn", wl.name) if packed else None
     roof.update({
         "kernel": "expert FFN grouped GEMM: the two launches (GEMM1, GEMM2) of one "
                   "moe_expert_ffn, timed together",
@@ -231,6 +255,8 @@ def main():
         "arithmetic_intensity": ai, "mfma_util": alg["ffn_flops"] / ffn_s / 1e12 / peak_flops,
         "avg_ms": t_ffn,
     })
+    if roof["traffic"] is not None:
+        roof["traffic_over_algorithmic"] = roof["traffic"] / alg["ffn_bytes"]
 
     res = {
         "metric": BASELINE_METRIC,

@@ -16,7 +16,7 @@
 //   gather kernel : x_disp[row] = x[row_token[row]] with 16-byte vectors
 // Up to kSmallDispatchRoutes routes (16-byte-vector rows) all three run as one
 // launch: every block histograms all A routes itself (the expert totals and
-// the counts before its own 32 routes), so no block waits on another.
+// the counts before its own 16 routes), so no block waits on another.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -229,8 +229,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
 }
 
 // The whole dispatch for A <= kSmallDispatchRoutes in one launch; block b
-// owns routes [32b, 32b + 32).
-constexpr int SBR = 32;
+// owns routes [16b, 16b + 16).
+constexpr int SBR = 16;
 __global__ __launch_bounds__(256) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, int A, int K, int E, int64_t cap,
     const u32x4* __restrict__ x, int row_vecs, int32_t* __restrict__ offsets,
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     }
   }
   __syncthreads();
-  copy_rows<SBR, 4>(x, xd, dst, src, row_vecs);
+  copy_rows<SBR, 8>(x, xd, dst, src, row_vecs);
 }
 
 // the same gather for rows that are not a whole number of 16-byte vectors

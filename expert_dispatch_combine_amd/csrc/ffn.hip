@@ -27,7 +27,8 @@
 //    tiles) and 32*WN weight rows, so each weight byte crosses HBM once.
 //    Weights go straight from global memory into a register ring PD chunks
 //    deep (no LDS); activations are shared by the 4 waves through a
-//    double-buffered, XOR-swizzled LDS tile, loaded two chunks ahead.  WK
+//    double-buffered, XOR-swizzled LDS tile, loaded two chunks ahead (four
+//    when a launch has at most one workgroup per CU).  WK
 //    waves split each 64-wide k-chunk when the weight dim is too short to
 //    give the chip enough work; their partial sums are added in LDS in a
 //    fixed order.
