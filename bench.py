@@ -77,6 +77,23 @@ def algorithmic(wl, R, E_nz):
     }
 
 
+def next_rows(M, bufs, torch, stream, reps=200):
+    """Per-call time (HIP events on `stream`, one pair per call, averaged) of
+    the entry points beyond the layer step, on the step's own buffers:
+    moe_bias_update (aux-loss-free balancing) on the step's routing."""
+    bias = torch.zeros((bufs.cfg.E,), dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            a.record(stream)
+            M.moe_bias_update(bufs.cfg, bufs.topk_idx, bias, 1e-3, None, stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    us = statistics.fmean(a.elapsed_time(b) for a, b in evs) * 1e3
+    return {"bias_update_us": us}
+
+
 def committed_traffic(kernel, workload):
     """HBM bytes per call of `kernel` on `workload` from the rocprofv3 counter
     summary committed under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled
@@ -286,6 +303,7 @@ def main():
         "ledger": {k: led[k] for k in ("accepted_routes", "overflow", "balance_ratio",
                                         "local_hit_ratio", "l_aux")},
     }
+    res["next_rows"] = next_rows(M, bufs, torch, main_s)
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, inp,
                                                                          args.cpu_seconds)
     print(json.dumps(res), flush=True)

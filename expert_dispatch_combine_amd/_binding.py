@@ -23,7 +23,7 @@ EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_capacity", "moe_max_rows", "moe_workspace_bytes",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_ledger",
     "moe_ledger_stage_bytes", "moe_ledger_launch", "moe_ledger_finalize",
-    "moe_expert_ffn_packed", "moe_pack_expert_weights",
+    "moe_expert_ffn_packed", "moe_pack_expert_weights", "moe_bias_update",
 )
 
 
@@ -115,6 +115,8 @@ def load_library():
     lib.moe_expert_ffn_packed.argtypes = [cfgp, _I64, P, P, P, P, P, P, P, P, P]
     lib.moe_pack_expert_weights.restype = ctypes.c_int
     lib.moe_pack_expert_weights.argtypes = [cfgp, P, P, P, P, P]
+    lib.moe_bias_update.restype = ctypes.c_int
+    lib.moe_bias_update.argtypes = [cfgp, P, P, ctypes.c_float, P, P]
     _lib = lib
     return lib
 
@@ -192,6 +194,16 @@ def moe_route(cfg: MoeCfg, x, w_gate, logit_bias, logits, topk_idx, topk_gate,
                        _ptr(topk_gate, "f32", cfg, "topk_gate"),
                        _ptr(expert_load, "i32", cfg, "expert_load"), wsp, wsb, _stream(stream))
     _check("moe_route", st)
+
+
+def moe_bias_update(cfg: MoeCfg, topk_idx, expert_bias, alpha: float = 0.1, counts=None,
+                    stream=None) -> None:
+    """expert_bias (fp32 [E], device) += alpha * (mean_count - count), in place."""
+    lib = load_library()
+    st = lib.moe_bias_update(ctypes.byref(cfg), _ptr(topk_idx, "i32", cfg, "topk_idx"),
+                             _ptr(expert_bias, "f32", cfg, "expert_bias"), float(alpha),
+                             _ptr(counts, "i32", cfg, "counts"), _stream(stream))
+    _check("moe_bias_update", st)
 
 
 def moe_dispatch(cfg: MoeCfg, x, topk_idx, capacity: int, expert_offsets, route_rank,

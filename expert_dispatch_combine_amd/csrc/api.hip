@@ -112,6 +112,16 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate, const float
       launch_topk_softmax(logits, logit_bias, topk_idx, topk_gate, expert_load, T, E, K, s));
 }
 
+int moe_bias_update(const moe_cfg* cfg, const int32_t* topk_idx, float* expert_bias,
+                    float alpha, int32_t* counts, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!expert_bias || !std::isfinite(alpha)) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && !topk_idx) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_bias_update(topk_idx, cfg->T, cfg->K, cfg->E, alpha, expert_bias,
+                                       counts, (hipStream_t)stream));
+}
+
 int moe_dispatch(const moe_cfg* cfg, const void* x, const int32_t* topk_idx, int64_t capacity,
                  int32_t* expert_offsets, int32_t* route_rank, int32_t* route_row,
                  int32_t* row_token, void* x_disp, int32_t* expert_load, void* ws,

@@ -68,6 +68,9 @@ inline size_t ledger_final_bytes(int E, int n_ep) {
 // Each returns hipSuccess or the first HIP error.
 hipError_t launch_router_gemm_bf16(const uint16_t* x, const uint16_t* wg, float* logits,
                                    int T, int h, int E, hipStream_t s);
+// bias[e] += alpha * (mean - count[e]), count = histogram of topk_idx[:, 0]
+hipError_t launch_bias_update(const int32_t* idx, int T, int K, int E, float alpha, float* bias,
+                              int32_t* counts, hipStream_t s);
 hipError_t launch_router_topk_bf16(const uint16_t* x, const uint16_t* wg, const float* bias,
                                    float* logits, int32_t* idx, float* gate, int32_t* load,
                                    int T, int h, int E, int K, hipStream_t s);

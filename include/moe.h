@@ -134,6 +134,22 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate,
               float* topk_gate, int32_t* expert_load, void* ws, size_t ws_bytes,
               void* stream);
 
+/* Aux-loss-free balancing: one step of the expert-bias rule of [DSV3]
+ * section 八 (DeepSeekV3Gate), bias += alpha * (mean_count - count), where
+ * count[e] = tokens whose largest bias-adjusted logit is expert e.
+ *   topk_idx    [T, K] int32  routing made by moe_route with
+ *                             logit_bias = expert_bias (slot 0 = argmax of
+ *                             the adjusted logits); ids outside [0, E) are
+ *                             not counted
+ *   expert_bias [E] fp32      updated in place (device memory)
+ *   alpha                     step size (the page uses 0.1); finite
+ *   counts      [E] int32|NULL  the per-expert counts used
+ * In fp32 with one rounding per operation and no fused multiply-add:
+ * mean = sum(count) / E, then per expert bias + alpha * (mean - count).
+ * Asynchronous on `stream`; one workgroup. */
+int moe_bias_update(const moe_cfg* cfg, const int32_t* topk_idx, float* expert_bias,
+                    float alpha, int32_t* counts, void* stream);
+
 /* Capacity-limited dispatch ([DSV3] 3.3 capacity loop; [EPC] Dispatch).
  * Routes are taken in (token, k-slot) order; the first `capacity` routes of
  * each expert are accepted and the rest dropped.  Accepted routes are packed
@@ -146,7 +162,11 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate,
  *                                left untouched)
  *   x_disp         [R_max, h] dtype  x_disp[row] = x[row_token[row]]
  *   expert_load    [E] int32|NULL    pre-capacity load of each expert
- * ws: at least moe_workspace_bytes(cfg) bytes. */
+ * ws: at least moe_workspace_bytes(cfg) bytes.
+ * Dropless variant: any capacity >= T accepts every route (a token's K
+ * experts are distinct, so no expert receives more than T routes); then
+ * R = T*K and R_max = T*K.  This is the dispatch that aux-loss-free
+ * balancing (moe_bias_update) pairs with ([DSV3] 3.3, section 八). */
 int moe_dispatch(const moe_cfg* cfg, const void* x, const int32_t* topk_idx,
                  int64_t capacity, int32_t* expert_offsets, int32_t* route_rank,
                  int32_t* route_row, int32_t* row_token, void* x_disp,

@@ -37,6 +37,12 @@ function that uses it):
       over accepted routes (the prose of [EP46] Step 2).
   R10 L_aux: the formula of [DSV3] 3.2 (alpha * sum f_i P_i) is `l_aux`; its
       code's normalisation (alpha * E * sum f_i P_i / K) is `l_aux_norm`.
+  R11 aux-loss-free balancing ([DSV3] section 八): the bias update counts each
+      token once, at the argmax of its adjusted logits (the top-1 expert, as
+      the page's bincount of argmax does), and applies
+      bias += alpha * (mean_count - count) with alpha = 0.1 in fp32, one
+      rounding per operation.  The dropless variant is the same dispatch with
+      a capacity of at least T (no expert can receive more than T routes).
 """
 from __future__ import annotations
 
@@ -51,7 +57,7 @@ __all__ = [
     "gelu_tanh", "expert_ffn", "expert_ffn_rows", "combine", "combine_index_add",
     "summarize_routes", "dispatch_locality", "aux_loss_terms",
     "uniform_expert_placement", "load_monitor", "ledger", "moe_layer",
-    "moe_layer_per_token", "routes_from_idx",
+    "moe_layer_per_token", "routes_from_idx", "top1_counts", "expert_bias_update",
 ]
 
 
@@ -549,3 +555,39 @@ def moe_layer_per_token(x, idx, gate, accepted_mask, w1, b1, w2, b2,
             y = round_f32(np.asarray(w2[e], np.float64) @ Hrow + np.asarray(b2[e], np.float64))
             out[t] += float(gate[t, k]) * y
     return round_f32(out)
+
+
+# ----------------------------------------------------------------------------
+# aux-loss-free balancing: the expert-bias update
+# ----------------------------------------------------------------------------
+def top1_counts(adjusted_logits32: np.ndarray) -> np.ndarray:
+    """count[e] = number of tokens whose largest adjusted logit is expert e
+    ([DSV3] section 八, DeepSeekV3Gate: bincount of the argmax over experts of
+    logits + expert_bias).  Equal logits: the lowest expert id, which is what
+    an argmax that returns the first maximum gives (reading R2)."""
+    a = np.asarray(adjusted_logits32, dtype=np.float64)
+    T, E = a.shape
+    counts = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        best = 0
+        for e in range(1, E):
+            if a[t, e] > a[t, best]:
+                best = e
+        counts[best] += 1
+    return counts
+
+
+def expert_bias_update(bias32, counts, alpha: float = 0.1) -> np.ndarray:
+    """One step of [DSV3] section 八's bias rule,
+        bias <- bias + alpha * (mean_count - count),
+    with the page's fp32 tensors: mean_count = fp32(sum(count) / E), then per
+    expert one fp32 subtraction, one fp32 product with fp32(alpha) and one
+    fp32 addition, each rounded (no fused multiply-add).  Returns the new
+    bias (fp32 values, as float64)."""
+    b = np.asarray(bias32, dtype=np.float32)
+    c = np.asarray(counts, dtype=np.float32)
+    E = b.shape[0]
+    mean = np.float32(np.float32(np.sum(np.asarray(counts, np.int64))) / np.float32(E))
+    diff = (mean - c).astype(np.float32)
+    step = (np.float32(alpha) * diff).astype(np.float32)
+    return (b + step).astype(np.float32).astype(np.float64)

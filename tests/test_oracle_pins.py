@@ -376,3 +376,61 @@ def test_load_monitor_alarm():
     m = O.load_monitor([30, 1, 1, 0])
     assert m["imbalanced"]
     assert math.isclose(m["var_over_mean"], float(np.var([30, 1, 1, 0], ddof=1)) / 8.0)
+
+
+# ------------------------------------------------- aux-loss-free bias update
+def test_top1_counts_match_argmax_bincount():
+    """[DSV3] section 八 counts tokens by bincount(argmax(adjusted logits));
+    torch's argmax returns the first maximum, i.e. the lower id on ties."""
+    rng = np.random.default_rng(11)
+    for T, E in [(1, 1), (50, 3), (200, 7), (333, 16)]:
+        logits = rng.integers(-2, 3, (T, E)).astype(np.float32)  # many ties
+        want = torch.bincount(torch.from_numpy(logits).argmax(-1), minlength=E).numpy()
+        assert np.array_equal(O.top1_counts(logits), want)
+
+
+def test_bias_update_closed_forms():
+    rng = np.random.default_rng(12)
+    E = 8
+    bias = rng.standard_normal(E).astype(np.float32)
+    # balanced counts: mean == count for every expert, the bias does not move
+    new = O.expert_bias_update(bias, np.full(E, 125), alpha=0.1)
+    assert np.array_equal(new, bias.astype(np.float64))
+    # every token on expert 0 (T = 1000): steps 0.1 * (125 - 1000) and 0.1 * 125
+    counts = np.zeros(E, np.int64)
+    counts[0] = 1000
+    new = O.expert_bias_update(bias, counts, alpha=0.1)
+    exact = bias.astype(np.float64) + 0.1 * (125.0 - counts)
+    ulp = np.spacing(np.abs(exact).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(new - exact) <= 2 * ulp + 1e-6)
+    assert new[0] < bias[0] and np.all(new[1:] > bias[1:])
+    # the steps cancel: sum(mean - count) = 0
+    counts = rng.integers(0, 500, E)
+    new = O.expert_bias_update(bias, counts, alpha=0.1)
+    assert abs(float(np.sum(new - bias))) <= 1e-3
+
+
+def test_bias_update_balances_a_skewed_router():
+    """The rule's purpose ([DSV3] 3.3 / section 八): iterating route -> count
+    -> update drives a Zipf-skewed top-1 routing toward equal loads.  The step
+    acts on raw token counts, so it must be small against them: with the
+    page's alpha = 0.1 and 2048 tokens the bias overshoots by tens of logits
+    per step (checked too); alpha = 1e-3 settles."""
+    rng = np.random.default_rng(13)
+    T, E = 2048, 16
+    perm = rng.permutation(E)
+    logits = (rng.standard_normal((T, E)) - 1.2 * np.log(perm + 1.0)).astype(np.float32)
+
+    def run(alpha, steps):
+        bias = np.zeros(E, np.float32)
+        ratios = []
+        for _ in range(steps):
+            counts = O.top1_counts(O.add_logit_bias(logits, bias))
+            ratios.append(counts.max() / (T / E))
+            bias = O.expert_bias_update(bias, counts, alpha=alpha).astype(np.float32)
+        return ratios
+
+    r = run(1e-3, 40)
+    assert r[0] > 3.0 and max(r[-5:]) < 1.2
+    r = run(0.1, 12)
+    assert max(r[-6:]) > 3.0  # oscillates: every token flips to one expert
