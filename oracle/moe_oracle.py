@@ -43,6 +43,10 @@ function that uses it):
       bias += alpha * (mean_count - count) with alpha = 0.1 in fp32, one
       rounding per operation.  The dropless variant is the same dispatch with
       a capacity of at least T (no expert can receive more than T routes).
+  R12 FP8 dispatch payload ([DSV3] 4.3): one scale for the whole [T, h]
+      activation tensor, scale = bf16(max|x| / 448); codes = E4M3(bf16(x /
+      scale)) with ties to even; the receiver's bf16(decode * scale) feeds the
+      experts.  All-zero activations (scale 0) give zero codes.
 """
 from __future__ import annotations
 
@@ -58,6 +62,7 @@ __all__ = [
     "summarize_routes", "dispatch_locality", "aux_loss_terms",
     "uniform_expert_placement", "load_monitor", "ledger", "moe_layer",
     "moe_layer_per_token", "routes_from_idx", "top1_counts", "expert_bias_update",
+    "E4M3_MAX", "e4m3_encode", "e4m3_decode", "fp8_scale", "fp8_quantize", "fp8_dequantize",
 ]
 
 
@@ -591,3 +596,72 @@ def expert_bias_update(bias32, counts, alpha: float = 0.1) -> np.ndarray:
     diff = (mean - c).astype(np.float32)
     step = (np.float32(alpha) * diff).astype(np.float32)
     return (b + step).astype(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# FP8 (OCP E4M3) dispatch payload
+# ----------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Round each value to the nearest E4M3 (1 sign, 4 exponent bits with bias
+    7, 3 mantissa bits; no infinities, code 0x7F/0xFF = NaN, largest finite
+    448), ties to even, as the 'to(float8_e4m3fn)' conversion of [DSV3] 4.3
+    does.  Magnitudes above 464 (past the midpoint to the next, missing,
+    step) become NaN; below 2^-6 the spacing is 2^-9 (subnormals).
+    Returns uint8 codes."""
+    v = np.asarray(v, dtype=np.float64)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    a = np.abs(v)
+    nan = np.isnan(a) | (a > 464.0)
+    a = np.where(nan, 0.0, a)
+    # a = f * 2^ex with f in [0.5, 1): the leading bit has weight 2^(ex-1)
+    _, ex = np.frexp(a)
+    lead = ex.astype(np.int64) - 1
+    normal = a >= 2.0 ** -6
+    # spacing: 2^(lead-3) for normals, 2^-9 below 2^-6; rint = ties to even
+    step_exp = np.where(normal, lead - 3, -9)
+    q = np.rint(np.ldexp(a, -step_exp)).astype(np.int64)
+    # normals: q in [8, 16]; 16 carries into the next binade
+    carry = normal & (q == 16)
+    lead = np.where(carry, lead + 1, lead)
+    q = np.where(carry, 8, q)
+    code = np.where(normal, ((lead + 7) << 3) | (q - 8), q)  # subnormal q = 0..8
+    code = np.where(nan, 0x7F, code)
+    return (sign | code).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """E4M3 code -> value (float64; NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes, dtype=np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return s * val
+
+
+def fp8_scale(x_bf16) -> float:
+    """Per-tensor scale of [DSV3] 4.3 on bf16 activations: amax = max |x|
+    (a bf16 value), scale = bf16(amax / 448) (bf16 tensor arithmetic: the
+    quotient is formed in fp32 and rounded to bf16)."""
+    amax = float(np.max(np.abs(np.asarray(x_bf16, np.float64)))) if np.size(x_bf16) else 0.0
+    return float(round_bf16(round_f32(amax / E4M3_MAX)))
+
+
+def fp8_quantize(x_bf16, scale: float) -> np.ndarray:
+    """codes = e4m3(bf16(x / scale)): the division in bf16 tensor arithmetic
+    (fp32 quotient rounded to bf16), then the E4M3 rounding.  A zero scale
+    (all-zero input) gives zero codes (reading: the page divides by it)."""
+    x = np.asarray(x_bf16, np.float64)
+    if scale == 0.0:
+        return np.zeros(x.shape, np.uint8)
+    return e4m3_encode(round_bf16(round_f32(x / scale)))
+
+
+def fp8_dequantize(codes, scale: float) -> np.ndarray:
+    """bf16(decode(code) * scale): the E4M3 value widened to bf16 (exact),
+    times the bf16 scale, rounded to bf16 ([DSV3] 4.3 dequantisation)."""
+    return round_bf16(round_f32(e4m3_decode(codes) * scale))

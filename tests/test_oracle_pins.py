@@ -434,3 +434,56 @@ def test_bias_update_balances_a_skewed_router():
     assert r[0] > 3.0 and max(r[-5:]) < 1.2
     r = run(0.1, 12)
     assert max(r[-6:]) > 3.0  # oscillates: every token flips to one expert
+
+
+# ------------------------------------------------------- FP8 dispatch payload
+def test_e4m3_codes_match_torch_float8():
+    """[DSV3] 4.3 converts with torch's float8_e4m3fn; the oracle's E4M3
+    rounding is checked against it on every code and on values across the
+    whole range (subnormals, ties, the 448/464 edge, overflow to NaN)."""
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(want), np.isnan(got))
+    assert np.array_equal(want[~np.isnan(want)], got[~np.isnan(got)])
+    rng = np.random.default_rng(21)
+    vals = rng.standard_normal(50000) * np.exp2(rng.integers(-14, 10, 50000))
+    vals = np.concatenate([vals, want[~np.isnan(want)],  # every finite code, and
+                           (want[1:120] + want[:119]) / 2,  # every midpoint (ties)
+                           [448, 449, 463, 464, 465, 480, 1e6, -464, -465, 0.0, -0.0]])
+    vals = vals.astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(vals.astype(np.float64)), ref)
+
+
+def test_fp8_payload_matches_the_pages_torch_expression():
+    """scale = x.abs().max() / 448; q = (x / scale).to(float8_e4m3fn);
+    back = q.to(bfloat16) * scale, all on bf16 tensors ([DSV3] 4.3)."""
+    rng = np.random.default_rng(22)
+    for shape, mag in [((64, 96), 1.0), ((7, 33), 1e-3), ((128, 64), 300.0), ((1, 16), 1.0)]:
+        x = torch.from_numpy((rng.standard_normal(shape) * mag).astype(np.float32)).to(
+            torch.bfloat16)
+        scale_t = x.abs().max() / 448.0
+        q_t = (x / scale_t).to(torch.float8_e4m3fn)
+        back_t = q_t.to(torch.bfloat16) * scale_t
+        x64 = x.to(torch.float64).numpy()
+        scale = O.fp8_scale(x64)
+        assert scale == float(scale_t)
+        q = O.fp8_quantize(x64, scale)
+        assert np.array_equal(q, q_t.view(torch.uint8).numpy())
+        assert np.array_equal(O.fp8_dequantize(q, scale), back_t.to(torch.float64).numpy())
+
+
+def test_fp8_round_trip_error_and_zero_input():
+    rng = np.random.default_rng(23)
+    x = O.round_bf16(rng.standard_normal((50, 128)))
+    scale = O.fp8_scale(x)
+    back = O.fp8_dequantize(O.fp8_quantize(x, scale), scale)
+    # E4M3 keeps 3 mantissa bits: half a step is 2^-4 relative for normals, 2^-10
+    # scale absolute in the subnormal range; plus the bf16 roundings
+    bound = 2.0 ** -4 * np.abs(x) + 2.0 ** -10 * scale + 2.0 ** -7 * np.abs(x)
+    assert np.all(np.abs(back - x) <= bound)
+    assert np.max(np.abs(x)) <= 448.0 * scale * (1 + 2.0 ** -7)
+    z = np.zeros((4, 16))
+    assert O.fp8_scale(z) == 0.0
+    assert not np.any(O.fp8_quantize(z, 0.0)) and not np.any(O.fp8_dequantize(O.fp8_quantize(z, 0.0), 0.0))
