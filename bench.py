@@ -77,21 +77,41 @@ def algorithmic(wl, R, E_nz):
     }
 
 
-def next_rows(M, bufs, torch, stream, reps=200):
-    """Per-call time (HIP events on `stream`, one pair per call, averaged) of
-    the entry points beyond the layer step, on the step's own buffers:
-    moe_bias_update (aux-loss-free balancing) on the step's routing."""
-    bias = torch.zeros((bufs.cfg.E,), dtype=torch.float32, device="cuda")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    with torch.cuda.stream(stream):
-        for a, b in evs:
-            a.record(stream)
-            M.moe_bias_update(bufs.cfg, bufs.topk_idx, bias, 1e-3, None, stream)
-            b.record(stream)
-    torch.cuda.synchronize()
-    us = statistics.fmean(a.elapsed_time(b) for a, b in evs) * 1e3
-    return {"bias_update_us": us}
+def next_rows(M, bufs, torch, stream, x, reps=200):
+    """Per-call time (HIP events on `stream`, one pair per call, averaged; an
+    upper bound that includes the launch) of the entry points beyond the
+    layer step, on the step's own buffers: moe_bias_update (aux-loss-free
+    balancing) and the FP8 payload (moe_fp8_scale, moe_dispatch_fp8,
+    moe_fp8_dequantize), with the dispatch payload bytes of both formats."""
+    cfg, b = bufs.cfg, bufs
+    bias = torch.zeros((cfg.E,), dtype=torch.float32, device="cuda")
+    calls = {"bias_update_us": lambda: M.moe_bias_update(cfg, b.topk_idx, bias, 1e-3, None,
+                                                         stream)}
+    out = {}
+    if cfg.dtype == M.MOE_BF16:
+        scale = torch.zeros((1,), dtype=torch.float32, device="cuda")
+        xq = torch.empty((max(b.r_max, 1), cfg.h), dtype=torch.uint8, device="cuda")
+        xd = torch.empty_like(b.x_disp)
+        calls["fp8_scale_us"] = lambda: M.moe_fp8_scale(cfg, x, scale, b.ws, stream)
+        calls["fp8_dispatch_us"] = lambda: M.moe_dispatch_fp8(
+            cfg, x, scale, b.topk_idx, b.capacity, b.expert_offsets, b.route_rank, b.route_row,
+            b.row_token, xq, None, b.ws, stream)
+        calls["fp8_dequantize_us"] = lambda: M.moe_fp8_dequantize(
+            cfg, b.capacity, xq, scale, b.expert_offsets, xd, stream)
+        R = int(b.expert_offsets[-1].item())
+        out["fp8_payload_bytes"] = R * cfg.h
+        out["bf16_payload_bytes"] = R * cfg.h * 2
+    for name, fn in calls.items():
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        with torch.cuda.stream(stream):
+            for a, e in evs:
+                a.record(stream)
+                fn()
+                e.record(stream)
+        torch.cuda.synchronize()
+        out[name] = statistics.fmean(a.elapsed_time(e) for a, e in evs) * 1e3
+    return out
 
 
 def committed_traffic(kernel, workload):
@@ -303,7 +323,7 @@ def main():
         "ledger": {k: led[k] for k in ("accepted_routes", "overflow", "balance_ratio",
                                         "local_hit_ratio", "l_aux")},
     }
-    res["next_rows"] = next_rows(M, bufs, torch, main_s)
+    res["next_rows"] = next_rows(M, bufs, torch, main_s, inp.x)
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, inp,
                                                                          args.cpu_seconds)
     print(json.dumps(res), flush=True)

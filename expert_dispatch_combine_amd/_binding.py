@@ -24,6 +24,7 @@ EXPORTED_SYMBOLS = (
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_ledger",
     "moe_ledger_stage_bytes", "moe_ledger_launch", "moe_ledger_finalize",
     "moe_expert_ffn_packed", "moe_pack_expert_weights", "moe_bias_update",
+    "moe_fp8_scale", "moe_dispatch_fp8", "moe_fp8_dequantize",
 )
 
 
@@ -117,6 +118,13 @@ def load_library():
     lib.moe_pack_expert_weights.argtypes = [cfgp, P, P, P, P, P]
     lib.moe_bias_update.restype = ctypes.c_int
     lib.moe_bias_update.argtypes = [cfgp, P, P, ctypes.c_float, P, P]
+    lib.moe_fp8_scale.restype = ctypes.c_int
+    lib.moe_fp8_scale.argtypes = [cfgp, P, P, P, ctypes.c_size_t, P]
+    lib.moe_dispatch_fp8.restype = ctypes.c_int
+    lib.moe_dispatch_fp8.argtypes = [cfgp, P, P, P, _I64, P, P, P, P, P, P, P, ctypes.c_size_t,
+                                     P]
+    lib.moe_fp8_dequantize.restype = ctypes.c_int
+    lib.moe_fp8_dequantize.argtypes = [cfgp, _I64, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -130,6 +138,7 @@ _WANT = {
     "act": None,  # activation dtype: checked against cfg.dtype
     "f32": torch.float32,
     "i32": torch.int32,
+    "u8": torch.uint8,
 }
 
 
@@ -204,6 +213,46 @@ def moe_bias_update(cfg: MoeCfg, topk_idx, expert_bias, alpha: float = 0.1, coun
                              _ptr(expert_bias, "f32", cfg, "expert_bias"), float(alpha),
                              _ptr(counts, "i32", cfg, "counts"), _stream(stream))
     _check("moe_bias_update", st)
+
+
+def moe_fp8_scale(cfg: MoeCfg, x, scale, ws, stream=None) -> None:
+    """scale[0] = bf16(max|x| / 448) (fp32 device tensor of one element)."""
+    lib = load_library()
+    wsp, wsb = _ws(ws)
+    st = lib.moe_fp8_scale(ctypes.byref(cfg), _ptr(x, "act", cfg, "x"),
+                           _ptr(scale, "f32", cfg, "scale"), wsp, wsb, _stream(stream))
+    _check("moe_fp8_scale", st)
+
+
+def moe_dispatch_fp8(cfg: MoeCfg, x, scale, topk_idx, capacity: int, expert_offsets,
+                     route_rank, route_row, row_token, x_disp_q, expert_load=None, ws=None,
+                     stream=None) -> None:
+    """moe_dispatch sending E4M3 codes: x_disp_q is a uint8 [R_max, h] tensor."""
+    lib = load_library()
+    wsp, wsb = _ws(ws)
+    st = lib.moe_dispatch_fp8(ctypes.byref(cfg), _ptr(x, "act", cfg, "x"),
+                              _ptr(scale, "f32", cfg, "scale"),
+                              _ptr(topk_idx, "i32", cfg, "topk_idx"), int(capacity),
+                              _ptr(expert_offsets, "i32", cfg, "expert_offsets"),
+                              _ptr(route_rank, "i32", cfg, "route_rank"),
+                              _ptr(route_row, "i32", cfg, "route_row"),
+                              _ptr(row_token, "i32", cfg, "row_token"),
+                              _ptr(x_disp_q, "u8", cfg, "x_disp_q"),
+                              _ptr(expert_load, "i32", cfg, "expert_load"), wsp, wsb,
+                              _stream(stream))
+    _check("moe_dispatch_fp8", st)
+
+
+def moe_fp8_dequantize(cfg: MoeCfg, capacity: int, x_disp_q, scale, expert_offsets, x_disp,
+                       stream=None) -> None:
+    """x_disp[r] = bf16(value(x_disp_q[r]) * scale) for the accepted rows."""
+    lib = load_library()
+    st = lib.moe_fp8_dequantize(ctypes.byref(cfg), int(capacity),
+                                _ptr(x_disp_q, "u8", cfg, "x_disp_q"),
+                                _ptr(scale, "f32", cfg, "scale"),
+                                _ptr(expert_offsets, "i32", cfg, "expert_offsets"),
+                                _ptr(x_disp, "act", cfg, "x_disp"), _stream(stream))
+    _check("moe_fp8_dequantize", st)
 
 
 def moe_dispatch(cfg: MoeCfg, x, topk_idx, capacity: int, expert_offsets, route_rank,

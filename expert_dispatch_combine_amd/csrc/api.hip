@@ -74,7 +74,9 @@ size_t moe_workspace_bytes(const moe_cfg* cfg) {
   const int64_t A = routes_of(cfg);
   size_t a = dispatch_ws_bytes(A, cfg->E);
   size_t b = ledger_ws_bytes(A, cfg->E, kMaxRanks);
-  return (a > b ? a : b) + 256;
+  size_t c = (size_t)kFp8AmaxBlocks * sizeof(uint32_t);  // moe_fp8_scale partials
+  size_t m = a > b ? a : b;
+  return (m > c ? m : c) + 256;
 }
 
 int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate, const float* logit_bias,
@@ -139,6 +141,55 @@ int moe_dispatch(const moe_cfg* cfg, const void* x, const int32_t* topk_idx, int
   return hip_status(launch_dispatch(x, topk_idx, A, cfg->K, cfg->E, capacity, row_bytes, rmax,
                                     expert_offsets, route_rank, route_row, row_token, x_disp,
                                     expert_load, ws, (hipStream_t)stream));
+}
+
+int moe_fp8_scale(const moe_cfg* cfg, const void* x, float* scale, void* ws, size_t ws_bytes,
+                  void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!scale || !ws) return MOE_ERR_INVALID_ARG;
+  if (cfg->T > 0 && (!x || !aligned16(x))) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe_workspace_bytes(cfg)) return MOE_ERR_SHAPE;
+  return hip_status(launch_fp8_scale((const uint16_t*)x, (int64_t)cfg->T * cfg->h, scale, ws,
+                                     (hipStream_t)stream));
+}
+
+int moe_dispatch_fp8(const moe_cfg* cfg, const void* x, const float* scale,
+                     const int32_t* topk_idx, int64_t capacity, int32_t* expert_offsets,
+                     int32_t* route_rank, int32_t* route_row, int32_t* row_token,
+                     uint8_t* x_disp_q, int32_t* expert_load, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (capacity < 0 || !scale) return MOE_ERR_INVALID_ARG;
+  const int64_t A = routes_of(cfg);
+  const int64_t rmax = rows_max(cfg, capacity);
+  if (!expert_offsets || !ws) return MOE_ERR_INVALID_ARG;
+  if (A > 0 && (!topk_idx || !route_rank || !route_row)) return MOE_ERR_INVALID_ARG;
+  if (rmax > 0 && (!x || !x_disp_q || !row_token)) return MOE_ERR_INVALID_ARG;
+  if (rmax > 0 && (!aligned16(x) || !aligned16(x_disp_q))) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe_workspace_bytes(cfg)) return MOE_ERR_SHAPE;
+  return hip_status(launch_dispatch(x, topk_idx, A, cfg->K, cfg->E, capacity,
+                                    (int64_t)cfg->h * 2, rmax, expert_offsets, route_rank,
+                                    route_row, row_token, x_disp_q, expert_load, ws,
+                                    (hipStream_t)stream, scale));
+}
+
+int moe_fp8_dequantize(const moe_cfg* cfg, int64_t capacity, const uint8_t* x_disp_q,
+                       const float* scale, const int32_t* expert_offsets, void* x_disp,
+                       void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  const int64_t rmax = rows_max(cfg, capacity);
+  if (rmax == 0) return MOE_OK;
+  if (!x_disp_q || !scale || !expert_offsets || !x_disp) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_disp_q) || !aligned16(x_disp)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_fp8_dequantize(x_disp_q, scale, expert_offsets, cfg->E, cfg->h, rmax,
+                                          (uint16_t*)x_disp, (hipStream_t)stream));
 }
 
 static int expert_ffn_common(const moe_cfg* cfg, int64_t capacity, const void* x_disp,

@@ -182,11 +182,15 @@ __global__ __launch_bounds__(256) void slot_kernel(
 
 // Copy NR token rows: xd[dst[r]] = x[src[r]] for r < NR with dst[r] >= 0
 // (row indices, in LDS).  The NR * row_vecs 16-byte vectors are spread over
-// the 256 threads; each thread issues U loads before their stores.
+// the 256 threads; each thread issues U loads before their stores.  With a
+// scale (FP8 payload) each 16-byte vector of eight bf16 becomes eight E4M3
+// codes (8 bytes) of the destination row.
 template <int NR, int U>
-__device__ __forceinline__ void copy_rows(const u32x4* __restrict__ x, u32x4* __restrict__ xd,
-                                          const int* dst, const int* src, int row_vecs) {
+__device__ __forceinline__ void copy_rows(const u32x4* __restrict__ x, void* __restrict__ xd,
+                                          const int* dst, const int* src, int row_vecs,
+                                          const float* __restrict__ q_scale) {
   const int nv = NR * row_vecs;
+  const float scale = q_scale ? *q_scale : 0.0f;
   for (int j0 = threadIdx.x; j0 < nv; j0 += 256 * U) {
     u32x4 v[U];
     int64_t to[U];
@@ -202,8 +206,11 @@ __device__ __forceinline__ void copy_rows(const u32x4* __restrict__ x, u32x4* __
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (to[u] >= 0) xd[to[u]] = v[u];
+    for (int u = 0; u < U; ++u) {
+      if (to[u] < 0) continue;
+      if (q_scale) ((uint2*)xd)[to[u]] = quantize8(v[u], scale);
+      else ((u32x4*)xd)[to[u]] = v[u];
+    }
   }
 }
 
@@ -214,7 +221,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
                                                      const int32_t* __restrict__ row_token,
                                                      const int32_t* __restrict__ offsets,
                                                      int E, int row_vecs,
-                                                     u32x4* __restrict__ xd) {
+                                                     void* __restrict__ xd,
+                                                     const float* __restrict__ q_scale) {
   __shared__ int dst[ROWS], src[ROWS];
   const int R = offsets[E];
   const int r0 = blockIdx.x * ROWS;
@@ -225,7 +233,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
     src[threadIdx.x] = r < R ? row_token[r] : 0;
   }
   __syncthreads();
-  copy_rows<ROWS, 8>(x, xd, dst, src, row_vecs);
+  copy_rows<ROWS, 8>(x, xd, dst, src, row_vecs, q_scale);
 }
 
 // The whole dispatch for A <= kSmallDispatchRoutes in one launch; block b
@@ -235,7 +243,8 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, int A, int K, int E, int64_t cap,
     const u32x4* __restrict__ x, int row_vecs, int32_t* __restrict__ offsets,
     int32_t* __restrict__ route_rank, int32_t* __restrict__ route_row,
-    int32_t* __restrict__ row_token, int32_t* __restrict__ load_out, u32x4* __restrict__ xd) {
+    int32_t* __restrict__ row_token, int32_t* __restrict__ load_out, void* __restrict__ xd,
+    const float* __restrict__ q_scale) {
   __shared__ int tot[kMaxExperts], bef[kMaxExperts], off[kMaxExperts + 1];
   __shared__ int sh_wave[4];
   __shared__ int dst[SBR], src[SBR];
@@ -310,7 +319,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     }
   }
   __syncthreads();
-  copy_rows<SBR, 8>(x, xd, dst, src, row_vecs);
+  copy_rows<SBR, 8>(x, xd, dst, src, row_vecs, q_scale);
 }
 
 // the same gather for rows that are not a whole number of 16-byte vectors
@@ -338,14 +347,15 @@ hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int64_t A, in
                            int64_t cap, int64_t row_bytes, int64_t r_max,
                            int32_t* offsets, int32_t* route_rank, int32_t* route_row,
                            int32_t* row_token, void* x_disp, int32_t* load, void* ws,
-                           hipStream_t s) {
+                           hipStream_t s, const float* q_scale) {
   const bool vec = row_bytes % 16 == 0 && ((uintptr_t)x & 15u) == 0 &&
                    ((uintptr_t)x_disp & 15u) == 0;
+  if (q_scale && !vec) return hipErrorInvalidValue;  // the FP8 path needs vector rows
   if (A > 0 && A <= kSmallDispatchRoutes && r_max > 0 && vec) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3((unsigned)((A + SBR - 1) / SBR)), dim3(256),
                        0, s, topk_idx, (int)A, K, E, cap, (const u32x4*)x,
                        (int)(row_bytes / 16), offsets, route_rank, route_row, row_token, load,
-                       (u32x4*)x_disp);
+                       x_disp, q_scale);
     return hipGetLastError();
   }
   const int nb = (int)((A + RPB - 1) / RPB);
@@ -364,8 +374,8 @@ hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int64_t A, in
     constexpr int ROWS = 16;
     const int64_t grid = (r_max + ROWS - 1) / ROWS;
     hipLaunchKernelGGL((gather_kernel<ROWS>), dim3((unsigned)grid), dim3(256), 0, s,
-                       (const u32x4*)x, row_token, offsets, E, (int)(row_bytes / 16),
-                       (u32x4*)x_disp);
+                       (const u32x4*)x, row_token, offsets, E, (int)(row_bytes / 16), x_disp,
+                       q_scale);
   } else {
     hipLaunchKernelGGL(gather_bytes_kernel, dim3((unsigned)r_max), dim3(256), 0, s,
                        (const uint8_t*)x, row_token, offsets, E, row_bytes,

@@ -281,11 +281,28 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
       _Pragma("unroll") for (int j = 0; j < MT; ++j) areg[ASLOT][j] =                 \
           *(const u32x4*)(ap[j] + ((c) + S::AD) * S::KC);                             \
     }                                                                                 \
-    _Pragma("unroll") for (int s = 0; s < S::KSTEPS; ++s) {                           \
-      const bf16x8 wa = __builtin_bit_cast(bf16x8, wr[SLOT][s]);                      \
-      _Pragma("unroll") for (int tm = 0; tm < MT; ++tm) {                             \
-        const bf16x8 xb = *(const bf16x8*)(stage_ + afrag[tm][s]);                    \
-        acc[tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, xb, acc[tm], 0, 0, 0);  \
+    if constexpr (OCC == 1) {                                                         \
+      /* one wave per SIMD: nothing else hides LDS latency, so every fragment */      \
+      /* of the chunk is read before the first MFMA (the scheduling barrier */        \
+      /* keeps the compiler from sinking the reads next to their uses) */             \
+      bf16x8 xf_[S::KSTEPS][MT];                                                      \
+      _Pragma("unroll") for (int s = 0; s < S::KSTEPS; ++s)                           \
+        _Pragma("unroll") for (int tm = 0; tm < MT; ++tm) xf_[s][tm] =                \
+            *(const bf16x8*)(stage_ + afrag[tm][s]);                                  \
+      __builtin_amdgcn_sched_barrier(0);                                              \
+      _Pragma("unroll") for (int s = 0; s < S::KSTEPS; ++s) {                         \
+        const bf16x8 wa = __builtin_bit_cast(bf16x8, wr[SLOT][s]);                    \
+        _Pragma("unroll") for (int tm = 0; tm < MT; ++tm)                             \
+          acc[tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, xf_[s][tm], acc[tm],   \
+                                                            0, 0, 0);                 \
+      }                                                                               \
+    } else {                                                                          \
+      _Pragma("unroll") for (int s = 0; s < S::KSTEPS; ++s) {                         \
+        const bf16x8 wa = __builtin_bit_cast(bf16x8, wr[SLOT][s]);                    \
+        _Pragma("unroll") for (int tm = 0; tm < MT; ++tm) {                           \
+          const bf16x8 xb = *(const bf16x8*)(stage_ + afrag[tm][s]);                  \
+          acc[tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, xb, acc[tm], 0, 0, 0); \
+        }                                                                             \
       }                                                                               \
     }                                                                                 \
     if (REFILL) {                                                                     \

@@ -81,11 +81,69 @@ hipError_t launch_topk_softmax(const float* logits, const float* bias, int32_t* 
                                float* gate, int32_t* load, int T, int E, int K,
                                hipStream_t s);
 
+// ---- OCP E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+// infinities; 0x7F/0xFF = NaN; largest finite 448), as in "MoE大模型专家并行与
+// 动态路由优化" 4.3 (FP8 all-to-all payload).
+
+// nearest E4M3 code, ties to even; magnitudes above 464 (and NaN) -> NaN code
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (!(a <= 464.0f)) return sign | 0x7Fu;
+  if (a < 0x1p-6f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);  // spacing 2^-9
+  int lead = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;            // a is normal
+  int q = (int)__builtin_rintf(__builtin_ldexpf(a, 3 - lead));           // 8 .. 16
+  if (q == 16) {
+    ++lead;
+    q = 8;
+  }
+  return sign | ((uint32_t)(lead + 7) << 3) | (uint32_t)(q - 8);
+}
+
+// value of an E4M3 code (never called on the NaN code by the quantiser's output)
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e == 0 ? (float)m * 0x1p-9f
+                           : __builtin_ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// eight bf16 (one 16-byte vector) -> eight E4M3 codes: code(bf16(x / scale));
+// a zero scale (all-zero activations) gives zero codes
+__device__ __forceinline__ uint2 quantize8(u32x4 v, float scale) {
+  uint32_t out[2] = {0u, 0u};
+  if (scale != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = v[i >> 1];
+      const float x = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      const float q = __uint_as_float(bf16_rne_bits(__fdiv_rn(x, scale)) << 16);
+      out[i >> 2] |= e4m3_code(q) << (8 * (i & 3));
+    }
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+// q_scale: NULL for a plain row copy, else the device address of the FP8
+// scale; then x holds bf16 rows and x_disp receives E4M3 codes (h bytes/row)
 hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int64_t A, int K, int E,
                            int64_t cap, int64_t row_bytes, int64_t r_max,
                            int32_t* offsets, int32_t* route_rank, int32_t* route_row,
                            int32_t* row_token, void* x_disp, int32_t* load, void* ws,
-                           hipStream_t s);
+                           hipStream_t s, const float* q_scale = nullptr);
+// FP8 payload: per-tensor scale = bf16(max|x| / 448) of n bf16 values
+// (partials in ws: at least kFp8AmaxBlocks floats), and the receiver's
+// dequantisation x_disp[r] = bf16(value(code) * scale) for r < offsets[E].
+constexpr int kFp8AmaxBlocks = 1024;
+hipError_t launch_fp8_scale(const uint16_t* x, int64_t n, float* scale, void* ws, hipStream_t s);
+hipError_t launch_fp8_dequantize(const uint8_t* xq, const float* scale, const int32_t* offsets,
+                                 int E, int h, int64_t r_max, uint16_t* x_disp, hipStream_t s);
 
 hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* offsets, const uint16_t* w1,
                            const float* b1, const uint16_t* w2, const float* b2,

@@ -134,6 +134,31 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate,
               float* topk_gate, int32_t* expert_load, void* ws, size_t ws_bytes,
               void* stream);
 
+/* FP8 (OCP E4M3) dispatch payload ([DSV3] 4.3: quantise the bf16 hidden
+ * states to FP8 before the all-to-all, dequantise after it).  bf16 only.
+ *
+ * moe_fp8_scale: scale[0] = bf16(max|x| / 448) over the whole [T, h] tensor
+ *   x (stored as the fp32 value of that bf16; 0 for all-zero x).  Uses the
+ *   workspace (moe_workspace_bytes).  Asynchronous.
+ * moe_dispatch_fp8: moe_dispatch whose gather sends E4M3 codes: x_disp_q
+ *   [R_max, h] uint8 receives code(bf16(x / scale)) (ties to even; zero codes
+ *   when scale == 0) of each accepted row; every other output as in
+ *   moe_dispatch.  x and x_disp_q 16-byte aligned.
+ * moe_fp8_dequantize: the receiver, x_disp[r] = bf16(value(code) * scale)
+ *   for the R = expert_offsets[E] accepted rows (read on the device); rows
+ *   >= R are left untouched.  Its output feeds moe_expert_ffn*.
+ * All three return MOE_ERR_UNSUPPORTED for fp32 configurations. */
+int moe_fp8_scale(const moe_cfg* cfg, const void* x, float* scale, void* ws,
+                  size_t ws_bytes, void* stream);
+int moe_dispatch_fp8(const moe_cfg* cfg, const void* x, const float* scale,
+                     const int32_t* topk_idx, int64_t capacity, int32_t* expert_offsets,
+                     int32_t* route_rank, int32_t* route_row, int32_t* row_token,
+                     uint8_t* x_disp_q, int32_t* expert_load, void* ws, size_t ws_bytes,
+                     void* stream);
+int moe_fp8_dequantize(const moe_cfg* cfg, int64_t capacity, const uint8_t* x_disp_q,
+                       const float* scale, const int32_t* expert_offsets, void* x_disp,
+                       void* stream);
+
 /* Aux-loss-free balancing: one step of the expert-bias rule of [DSV3]
  * section 八 (DeepSeekV3Gate), bias += alpha * (mean_count - count), where
  * count[e] = tokens whose largest bias-adjusted logit is expert e.

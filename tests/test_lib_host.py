@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(moe_[a-z_]+)\s*\(", src,
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(moe_[a-z_0-9]+)\s*\(", src,
                                  flags=re.M)))
 
 
@@ -106,6 +106,20 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
                           ctypes.byref(out), None, None, None, None, None, 0, None) == 1
     assert lib.moe_ledger(ctypes.byref(cfg), None, None, None, 2, None, None, 2, 0.01,
                           None, None, None, None, None, None, 0, None) == 1
+    # bias update: NULL bias, non-finite alpha
+    assert lib.moe_bias_update(ctypes.byref(cfg), None, None, 0.1, None, None) == 1
+    assert lib.moe_bias_update(ctypes.byref(cfg), None, ctypes.c_void_p(16),
+                               float("nan"), None, None) == 1
+    # FP8 payload: fp32 configurations are unsupported; NULL scale / workspace
+    cfg32 = mk(4, 64, 2, 1, 64, "f32", 1.0)
+    assert lib.moe_fp8_scale(ctypes.byref(cfg32), None, None, None, 0, None) == 5
+    assert lib.moe_dispatch_fp8(ctypes.byref(cfg32), None, None, None, 2, None, None, None,
+                                None, None, None, None, 0, None) == 5
+    assert lib.moe_fp8_dequantize(ctypes.byref(cfg32), 2, None, None, None, None, None) == 5
+    assert lib.moe_fp8_scale(ctypes.byref(cfg), None, None, None, 0, None) == 1
+    assert lib.moe_dispatch_fp8(ctypes.byref(cfg), None, None, None, 2, None, None, None,
+                                None, None, None, None, 0, None) == 1
+    assert lib.moe_fp8_dequantize(ctypes.byref(cfg), 2, None, None, None, None, None) == 1
 
 
 def test_empty_batch_needs_no_device_work(lib):
