@@ -114,6 +114,44 @@ def next_rows(M, bufs, torch, stream, x, reps=200):
     return out
 
 
+def routing_scenarios(M, W, torch, stream, reps=200):
+    """The expert-parallel mechanism workload of the pages (2 ranks x 256
+    tokens, h 1024, 4 experts, top-2, cf 1.25, bf16) under its three routing
+    scenarios: the whole step (logits-in route, dispatch, FFN, combine,
+    ledger) per scenario, its average time, the ledger's locality / overflow /
+    balance and the plan decision."""
+    from expert_dispatch_combine_amd.runner import LayerBuffers, LayerPlan, capacity_of, cfg_from
+    cfg = W.SCENARIO_CONFIG
+    inp = W.make_inputs(cfg, "cuda")
+    mc = cfg_from(cfg)
+    b = LayerBuffers(mc, capacity_of(mc), "cuda")
+    w1, w2 = inp.w1, inp.w2
+    out = {"workload": f"{cfg.name}: T={cfg.T} h={cfg.h} E={cfg.E} K={cfg.K} F={cfg.F} "
+                       f"cf={cfg.cf} n_ep={cfg.n_ep}"}
+    for name in W.ROUTING_SCENARIOS:
+        b.logits.copy_(torch.from_numpy(W.scenario_logits(name)))
+        plan = LayerPlan(b, inp.x, inp.w_gate, None, w1, inp.b1, w2, inp.b2, inp.src_rank,
+                         inp.owner_rank, cfg.n_ep, main=stream, logits_in=True)
+        with torch.cuda.stream(stream):
+            for _ in range(10):
+                plan.launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                plan.launch()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        led = plan.ledger()
+        out[name] = {"step_us": e0.elapsed_time(e1) * 1e3 / reps,
+                     "local_hit_ratio": led["local_hit_ratio"],
+                     "cross_rank_dispatch_bytes": led["cross_rank_dispatch_bytes"],
+                     "overflow": led["overflow"], "balance_ratio": led["balance_ratio"],
+                     "plan": M.moe_recommend_plan(led)}
+    return out
+
+
 def committed_traffic(kernel, workload):
     """HBM bytes per call of `kernel` on `workload` from the rocprofv3 counter
     summary committed under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled
@@ -324,6 +362,7 @@ def main():
                                         "local_hit_ratio", "l_aux")},
     }
     res["next_rows"] = next_rows(M, bufs, torch, main_s, inp.x)
+    res["next_rows"]["routing_scenarios"] = routing_scenarios(M, W, torch, main_s)
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, inp,
                                                                          args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -24,7 +24,7 @@ EXPORTED_SYMBOLS = (
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_ledger",
     "moe_ledger_stage_bytes", "moe_ledger_launch", "moe_ledger_finalize",
     "moe_expert_ffn_packed", "moe_pack_expert_weights", "moe_bias_update",
-    "moe_fp8_scale", "moe_dispatch_fp8", "moe_fp8_dequantize",
+    "moe_fp8_scale", "moe_dispatch_fp8", "moe_fp8_dequantize", "moe_recommend_plan",
 )
 
 
@@ -123,6 +123,9 @@ def load_library():
     lib.moe_dispatch_fp8.restype = ctypes.c_int
     lib.moe_dispatch_fp8.argtypes = [cfgp, P, P, P, _I64, P, P, P, P, P, P, P, ctypes.c_size_t,
                                      P]
+    lib.moe_recommend_plan.restype = ctypes.c_int
+    lib.moe_recommend_plan.argtypes = [ctypes.POINTER(MoeLedger), ctypes.POINTER(_F64),
+                                       ctypes.c_int32]
     lib.moe_fp8_dequantize.restype = ctypes.c_int
     lib.moe_fp8_dequantize.argtypes = [cfgp, _I64, P, P, P, P, P]
     _lib = lib
@@ -393,3 +396,23 @@ def moe_ledger_finalize(cfg: MoeCfg, capacity: int, n_ep: int, alpha: float,
     d["pair_routes"] = [list(pair[i * n_ep:(i + 1) * n_ep]) for i in range(n_ep)]
     d["return_status"] = st
     return d
+
+
+PLAN_NAMES = ("accept", "tune", "reject")
+
+
+def moe_recommend_plan(ledger: dict, thresholds=None, use_locality: bool = True) -> str:
+    """Joint plan decision over a ledger dict (as moe_ledger returns):
+    'accept' / 'tune' / 'reject'.  thresholds: None (the page's limits) or
+    5 numbers (accept balance, accept cross share, tune overflow share, tune
+    balance, tune cross share)."""
+    lib = load_library()
+    L = MoeLedger()
+    for name, _ in MoeLedger._fields_:
+        setattr(L, name, ledger[name])
+    th = None if thresholds is None else (_F64 * 5)(*[float(v) for v in thresholds])
+    r = lib.moe_recommend_plan(ctypes.byref(L), th, int(bool(use_locality)))
+    if r < 0:
+        raise MoeError("moe_recommend_plan", 1)
+    return PLAN_NAMES[r]
+

@@ -402,6 +402,23 @@ int moe_ledger_finalize(const moe_cfg* cfg, int64_t capacity, int32_t n_ep, doub
 }
 
 
+int moe_recommend_plan(const moe_ledger_t* L, const double* thresholds, int32_t use_locality) {
+  if (!L) return -1;
+  // limits: accept balance, accept cross-rank share, tune overflow share,
+  // tune balance, tune cross-rank share
+  static const double kPageLimits[5] = {1.2, 0.5, 0.25, 1.8, 0.9};
+  const double* th = thresholds ? thresholds : kPageLimits;
+  if (L->total_routes <= 0) return MOE_PLAN_REJECT;
+  const double overflow_share = (double)L->overflow / (double)L->total_routes;
+  const int64_t loc_total = L->local_routes + L->cross_rank_routes;
+  const double cross =
+      (use_locality && loc_total > 0) ? (double)L->cross_rank_routes / (double)loc_total : 0.0;
+  if (L->overflow == 0 && L->balance_ratio <= th[0] && cross <= th[1]) return MOE_PLAN_ACCEPT;
+  if (overflow_share <= th[2] && L->balance_ratio <= th[3] && cross <= th[4])
+    return MOE_PLAN_TUNE;
+  return MOE_PLAN_REJECT;
+}
+
 int moe_ledger(const moe_cfg* cfg, const int32_t* topk_idx, const float* topk_gate,
                const int32_t* route_row, int64_t capacity, const int32_t* src_rank,
                const int32_t* owner_rank, int32_t n_ep, double alpha, moe_ledger_t* out,

@@ -103,11 +103,13 @@ class LayerPlan:
     `ledger()` decodes the stage on the host.
 
     The plan does not own the tensors: they must outlive it and keep their
-    storage (a HIP graph captured from launch() replays these addresses)."""
+    storage (a HIP graph captured from launch() replays these addresses).
+    logits_in: route from the logits already in `b.logits` (moe_route with
+    x = NULL) instead of the router product."""
 
     def __init__(self, b: LayerBuffers, x, w_gate, logit_bias, w1, b1, w2, b2, src_rank,
                  owner_rank, n_ep: int, alpha: float = 0.01, main=None, side=None,
-                 ledger_ws=None, packed: bool = False):
+                 ledger_ws=None, packed: bool = False, logits_in: bool = False):
         lib = load_library()
         cfg = b.cfg
         self.b, self.cfg, self.n_ep, self.alpha = b, cfg, int(n_ep), float(alpha)
@@ -125,7 +127,8 @@ class LayerPlan:
         self._cfg_ref = cfg  # byref() keeps no reference of its own
         self._keep = (x, w_gate, logit_bias, w1, b1, w2, b2, src_rank, owner_rank)
         p = lambda t, k, n: _ptr(t, k, cfg, n)  # noqa: E731
-        self.route = (lib.moe_route, (c, p(x, "act", "x"), p(w_gate, "act", "w_gate"),
+        rx, rw = (None, None) if logits_in else (x, w_gate)  # logits_in: b.logits is the input
+        self.route = (lib.moe_route, (c, p(rx, "act", "x"), p(rw, "act", "w_gate"),
                                       p(logit_bias, "f32", "logit_bias"),
                                       p(b.logits, "f32", "logits"),
                                       p(b.topk_idx, "i32", "topk_idx"),

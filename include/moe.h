@@ -279,6 +279,22 @@ int moe_ledger_finalize(const moe_cfg* cfg, int64_t capacity, int32_t n_ep, doub
                         const void* host_stage, moe_ledger_t* out, int64_t* loads,
                         double* f, double* P, int64_t* pair_routes);
 
+/* Joint parallel-plan decision over one ledger ([EP46] TODO 3, joint
+ * decision; thresholds default to that page's):
+ *   MOE_PLAN_ACCEPT  no overflow, balance_ratio <= 1.2 and cross-rank share
+ *                    <= 0.5;
+ *   MOE_PLAN_TUNE    overflow / total_routes <= 0.25, balance_ratio <= 1.8 and
+ *                    cross-rank share <= 0.9;
+ *   MOE_PLAN_REJECT  otherwise, and for an empty batch.
+ * The cross-rank share is cross_rank_routes / (local_routes +
+ * cross_rank_routes) (all routes) when use_locality != 0, else 0.
+ * thresholds: NULL, or 5 doubles in the order above (accept balance, accept
+ * cross share, tune overflow share, tune balance, tune cross share).
+ * Pure host function; returns -1 for a NULL ledger. */
+enum { MOE_PLAN_ACCEPT = 0, MOE_PLAN_TUNE = 1, MOE_PLAN_REJECT = 2 };
+int moe_recommend_plan(const moe_ledger_t* ledger, const double* thresholds,
+                       int32_t use_locality);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ import numpy as np
 import torch
 
 __all__ = ["Config", "CONFIGS", "custom", "make_inputs", "Inputs", "host_f64",
-           "seed_for"]
+           "seed_for", "ROUTING_SCENARIOS", "SCENARIO_CONFIG", "scenario_logits"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -79,7 +79,7 @@ def custom(T, h, E, K, F, cf=1.0, dtype="bf16", n_ep=2, src_rank="mod",
 
 
 # tensor ids: one child stream per tensor (and per expert for W1/W2)
-_TID = {"x": 0, "w_gate": 1, "w1": 2, "b1": 3, "w2": 4, "b2": 5, "perm": 6}
+_TID = {"x": 0, "w_gate": 1, "w1": 2, "b1": 3, "w2": 4, "b2": 5, "perm": 6, "logits": 7}
 
 
 def seed_for(seed: int, tensor: str, expert: int = -1) -> int:
@@ -152,3 +152,37 @@ def host_f64(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
     if t is None:
         return None
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+# ----------------------------------------------------------------------------
+# routing scenarios of the expert-parallel mechanism benchmark
+# ----------------------------------------------------------------------------
+# "46. MoE Expert Parallel" Step 5 fixes the workload (2 ranks, 256 tokens per
+# rank, hidden 1024, 4 experts, top-2, capacity factor 1.25, bf16) and varies
+# only the routing: local-heavy, balanced, skewed.  The page does not say how
+# each routing is drawn; here the router logits are seeded N(0, 1) plus a
+# per-scenario bias: +4 on the experts owned by the token's source rank
+# (local_heavy), none (balanced), +3 on expert 0 (skewed).  Experts are owned
+# round robin (e % 2); tokens come from ranks in contiguous blocks of 256.
+# The FFN width (not given) is 4 * hidden.
+ROUTING_SCENARIOS = ("local_heavy", "balanced", "skewed")
+SCENARIO_CONFIG = Config("ep-mechanism-bf16", T=512, h=1024, E=4, K=2, F=4096, cf=1.25,
+                         dtype="bf16", n_ep=2, src_rank="block", seed=1046)
+
+
+def scenario_logits(name: str, cfg: Config = SCENARIO_CONFIG) -> np.ndarray:
+    """fp32 router logits [T, E] of one routing scenario (seeded)."""
+    if name not in ROUTING_SCENARIOS:
+        raise ValueError(f"unknown routing scenario {name!r}")
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_for(cfg.seed, "logits", ROUTING_SCENARIOS.index(name)))
+    logits = torch.randn((cfg.T, cfg.E), generator=g, dtype=torch.float32)
+    t = torch.arange(cfg.T)
+    src = (t * cfg.n_ep) // cfg.T
+    owner = torch.arange(cfg.E) % cfg.n_ep
+    if name == "local_heavy":
+        logits += 4.0 * (owner[None, :] == src[:, None]).to(torch.float32)
+    elif name == "skewed":
+        logits[:, 0] += 3.0
+    return logits.numpy()
+

@@ -63,6 +63,7 @@ __all__ = [
     "uniform_expert_placement", "load_monitor", "ledger", "moe_layer",
     "moe_layer_per_token", "routes_from_idx", "top1_counts", "expert_bias_update",
     "E4M3_MAX", "e4m3_encode", "e4m3_decode", "fp8_scale", "fp8_quantize", "fp8_dequantize",
+    "PLAN_THRESHOLDS", "recommend_plan",
 ]
 
 
@@ -665,3 +666,36 @@ def fp8_dequantize(codes, scale: float) -> np.ndarray:
     """bf16(decode(code) * scale): the E4M3 value widened to bf16 (exact),
     times the bf16 scale, rounded to bf16 ([DSV3] 4.3 dequantisation)."""
     return round_bf16(round_f32(e4m3_decode(codes) * scale))
+
+
+# ----------------------------------------------------------------------------
+# the joint parallel-plan decision over the ledger
+# ----------------------------------------------------------------------------
+PLAN_THRESHOLDS = {"max_accept_balance": 1.2, "max_accept_cross_rank": 0.5,
+                   "max_tune_overflow_ratio": 0.25, "max_tune_balance": 1.8,
+                   "max_tune_cross_rank": 0.9}
+
+
+def recommend_plan(summary: dict, locality: Optional[dict] = None, **thresholds) -> str:
+    """[EP46] TODO 3 (joint decision): 'accept' when nothing overflows and
+    both the load balance ratio and the cross-rank share of routes stay within
+    the accept limits; 'tune' when the overflow share, the balance ratio and
+    the cross-rank share all stay within the (looser) tune limits; 'reject'
+    otherwise, and for an empty batch.  Without a locality summary the
+    cross-rank share counts as 0.  Limits default to the page's values."""
+    th = dict(PLAN_THRESHOLDS, **thresholds)
+    A = summary["total_routes"]
+    if A == 0:
+        return "reject"
+    overflow_share = summary["overflow"] / A
+    cross = 0.0
+    if locality is not None and locality["total_routes"]:
+        cross = locality["cross_rank_routes"] / locality["total_routes"]
+    bal = summary["balance_ratio"]
+    if (summary["overflow"] == 0 and bal <= th["max_accept_balance"]
+            and cross <= th["max_accept_cross_rank"]):
+        return "accept"
+    if (overflow_share <= th["max_tune_overflow_ratio"] and bal <= th["max_tune_balance"]
+            and cross <= th["max_tune_cross_rank"]):
+        return "tune"
+    return "reject"

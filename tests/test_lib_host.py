@@ -136,3 +136,44 @@ def test_ledger_struct_layout_matches_header(lib):
     # 20 int64 + 8 double + 2 int32
     assert ctypes.sizeof(M.MoeLedger) == 20 * 8 + 8 * 8 + 2 * 4
     assert ctypes.sizeof(M.MoeCfg) == 6 * 4 + 8
+
+
+def test_recommend_plan_matches_the_oracle(lib):
+    """The library's decision equals the oracle's on the page's contract cases
+    and on random ledgers around every limit (pure host function)."""
+    import json
+    import random
+    import oracle as O
+    from conftest import GOLDEN
+    g = json.load(open(os.path.join(GOLDEN, "ep46_decision_cases.json")))
+    for case in g["cases"]:
+        s = O.summarize_routes(case["routes"], case["num_experts"], case["hidden_size"])
+        led = {name: 0 for name, _ in M.MoeLedger._fields_}
+        led.update(total_routes=s["total_routes"], overflow=s["overflow"],
+                   balance_ratio=s["balance_ratio"])
+        loc = case["locality"]
+        if loc is not None:
+            led.update(local_routes=loc["local_routes"], cross_rank_routes=loc["cross_rank_routes"])
+        assert M.moe_recommend_plan(led, use_locality=loc is not None) == case["expect"]
+    rng = random.Random(9)
+    for _ in range(3000):
+        A = rng.choice([0, 1, 7, 100, 1000])
+        ovf = rng.randint(0, A)
+        bal = rng.choice([1.0, 1.2, 1.2000001, 1.5, 1.8, 1.8000001, 2.5])
+        cross = rng.randint(0, A)
+        led = {name: 0 for name, _ in M.MoeLedger._fields_}
+        led.update(total_routes=A, overflow=ovf, balance_ratio=bal, local_routes=A - cross,
+                   cross_rank_routes=cross)
+        want = O.recommend_plan({"total_routes": A, "overflow": ovf, "balance_ratio": bal},
+                                {"total_routes": A, "local_routes": A - cross,
+                                 "cross_rank_routes": cross})
+        assert M.moe_recommend_plan(led) == want
+    th = [1.0, 0.1, 0.5, 3.0, 1.0]
+    led = {name: 0 for name, _ in M.MoeLedger._fields_}
+    led.update(total_routes=10, overflow=0, balance_ratio=1.1, local_routes=9,
+               cross_rank_routes=1)
+    assert M.moe_recommend_plan(led, th) == O.recommend_plan(
+        {"total_routes": 10, "overflow": 0, "balance_ratio": 1.1},
+        {"total_routes": 10, "local_routes": 9, "cross_rank_routes": 1},
+        max_accept_balance=1.0, max_accept_cross_rank=0.1, max_tune_overflow_ratio=0.5,
+        max_tune_balance=3.0, max_tune_cross_rank=1.0)

@@ -487,3 +487,32 @@ def test_fp8_round_trip_error_and_zero_input():
     z = np.zeros((4, 16))
     assert O.fp8_scale(z) == 0.0
     assert not np.any(O.fp8_quantize(z, 0.0)) and not np.any(O.fp8_dequantize(O.fp8_quantize(z, 0.0), 0.0))
+
+
+# -------------------------------------------------------------- plan decision
+def test_plan_decision_page_contract():
+    g = _load("ep46_decision_cases.json")
+    assert O.PLAN_THRESHOLDS == g["source"]["thresholds"]
+    for case in g["cases"]:
+        s = O.summarize_routes(case["routes"], case["num_experts"], case["hidden_size"])
+        assert O.recommend_plan(s, case["locality"]) == case["expect"], case["name"]
+
+
+def test_plan_decision_boundaries():
+    """Each limit is inclusive, and crossing any one of them moves the plan."""
+    def summ(A, overflow, bal):
+        return {"total_routes": A, "overflow": overflow, "balance_ratio": bal}
+
+    def loc(cross, total=100):
+        return {"total_routes": total, "local_routes": total - cross, "cross_rank_routes": cross}
+
+    assert O.recommend_plan(summ(0, 0, 0.0)) == "reject"
+    assert O.recommend_plan(summ(100, 0, 1.2), loc(50)) == "accept"
+    assert O.recommend_plan(summ(100, 0, 1.2 + 1e-12), loc(50)) == "tune"
+    assert O.recommend_plan(summ(100, 0, 1.0), loc(51)) == "tune"
+    assert O.recommend_plan(summ(100, 1, 1.0), loc(0)) == "tune"
+    assert O.recommend_plan(summ(100, 25, 1.8), loc(90)) == "tune"
+    assert O.recommend_plan(summ(100, 26, 1.0), loc(0)) == "reject"
+    assert O.recommend_plan(summ(100, 0, 1.8 + 1e-12), loc(0)) == "reject"
+    assert O.recommend_plan(summ(100, 0, 1.0), loc(91)) == "reject"
+    assert O.recommend_plan(summ(100, 0, 1.0), loc(0, total=0)) == "accept"
