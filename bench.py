@@ -59,6 +59,9 @@ def parse():
                    help="run the ledger's kernels on a side stream beside the FFN, or after "
                         "the combine on the main stream")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-next-rows", action="store_true",
+                   help="skip the timings of the entry points beyond the layer step (bias "
+                        "update, FP8 payload, routing scenarios), e.g. under a profiler")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="rough budget of the CPU-oracle baseline")
     return p.parse_args()
@@ -120,18 +123,19 @@ def routing_scenarios(M, W, torch, stream, reps=200):
     scenarios: the whole step (logits-in route, dispatch, FFN, combine,
     ledger) per scenario, its average time, the ledger's locality / overflow /
     balance and the plan decision."""
-    from expert_dispatch_combine_amd.runner import LayerBuffers, LayerPlan, capacity_of, cfg_from
+    from expert_dispatch_combine_amd.runner import (LayerBuffers, LayerPlan, capacity_of,
+                                                    cfg_from, pack_weights)
     cfg = W.SCENARIO_CONFIG
     inp = W.make_inputs(cfg, "cuda")
     mc = cfg_from(cfg)
     b = LayerBuffers(mc, capacity_of(mc), "cuda")
-    w1, w2 = inp.w1, inp.w2
+    w1, w2 = pack_weights(mc, inp.w1, inp.w2)
     out = {"workload": f"{cfg.name}: T={cfg.T} h={cfg.h} E={cfg.E} K={cfg.K} F={cfg.F} "
                        f"cf={cfg.cf} n_ep={cfg.n_ep}"}
     for name in W.ROUTING_SCENARIOS:
         b.logits.copy_(torch.from_numpy(W.scenario_logits(name)))
         plan = LayerPlan(b, inp.x, inp.w_gate, None, w1, inp.b1, w2, inp.b2, inp.src_rank,
-                         inp.owner_rank, cfg.n_ep, main=stream, logits_in=True)
+                         inp.owner_rank, cfg.n_ep, main=stream, logits_in=True, packed=True)
         with torch.cuda.stream(stream):
             for _ in range(10):
                 plan.launch()
@@ -361,8 +365,9 @@ def main():
         "ledger": {k: led[k] for k in ("accepted_routes", "overflow", "balance_ratio",
                                         "local_hit_ratio", "l_aux")},
     }
-    res["next_rows"] = next_rows(M, bufs, torch, main_s, inp.x)
-    res["next_rows"]["routing_scenarios"] = routing_scenarios(M, W, torch, main_s)
+    if not args.no_next_rows:
+        res["next_rows"] = next_rows(M, bufs, torch, main_s, inp.x)
+        res["next_rows"]["routing_scenarios"] = routing_scenarios(M, W, torch, main_s)
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, inp,
                                                                          args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
 
   u32x4 wr[S::PD][S::KSTEPS];
 #pragma unroll
-  for (int p = 0; p < S::PD; ++p)
+  for (int p = 0; p < S::PD - 1; ++p)
     if (p < nchunks)
 #pragma unroll
       for (int q = 0; q < S::KSTEPS; ++q) wr[p][q] = *(const u32x4*)(wp + p * CSTR + q * QSTR);
@@ -268,10 +268,12 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
   __syncthreads();
 
   // One k-chunk c (PD is a multiple of AD and of 2, so every slot index is
-  // compile-time): issue the activations of chunk c+AD into slot c%AD, MFMAs
-  // on chunk c (weights from ring slot SLOT, activations from LDS stage STG),
-  // refill the weight slot with chunk c+PD, stage chunk c+1 (register slot
-  // (c+1)%AD, loaded AD-1 chunks earlier) into the other LDS buffer.  In the
+  // compile-time): issue the activations of chunk c+AD into slot c%AD and
+  // the weights of chunk c+PD-1 into the ring slot freed by chunk c-1 (both
+  // before the MFMAs, so the memory pipe stays fed while they run), MFMAs on
+  // chunk c (weights from ring slot SLOT, activations from LDS stage STG),
+  // stage chunk c+1 (register slot (c+1)%AD, loaded AD-1 chunks earlier) into
+  // the other LDS buffer.  In the
   // steady-state loop every condition is compile-time true, so the body has
   // no branches and the compiler counts the loads in flight exactly.
 #define MOE_STREAM_CHUNK(SLOT, STG, ASLOT, NSLOT, c, HAS_NEXT, HAS_NEXTA, REFILL)      \
@@ -280,6 +282,11 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     if (HAS_NEXTA) {                                                                  \
       _Pragma("unroll") for (int j = 0; j < MT; ++j) areg[ASLOT][j] =                 \
           *(const u32x4*)(ap[j] + ((c) + S::AD) * S::KC);                             \
+    }                                                                                 \
+    if (REFILL) {                                                                     \
+      _Pragma("unroll") for (int q = 0; q < S::KSTEPS; ++q)                           \
+        wr[((SLOT) + S::PD - 1) % S::PD][q] =                                         \
+            *(const u32x4*)(wp + ((c) + S::PD - 1) * CSTR + q * QSTR);                \
     }                                                                                 \
     if constexpr (OCC == 1) {                                                         \
       /* one wave per SIMD: nothing else hides LDS latency, so every fragment */      \
@@ -305,10 +312,6 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
         }                                                                             \
       }                                                                               \
     }                                                                                 \
-    if (REFILL) {                                                                     \
-      _Pragma("unroll") for (int q = 0; q < S::KSTEPS; ++q) wr[SLOT][q] =             \
-          *(const u32x4*)(wp + ((c) + S::PD) * CSTR + q * QSTR);                      \
-    }                                                                                 \
     if (HAS_NEXT) {                                                                   \
       uint16_t* nst_ = act + ((STG) ^ 1) * S::STAGE;                                  \
       _Pragma("unroll") for (int j = 0; j < MT; ++j) *(u32x4*)(nst_ + alds[j]) =      \
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     __syncthreads();                                                                  \
   } while (0)
 
-  // steady state: chunks c+1, c+AD and c+PD all exist (PD >= AD)
+  // steady state: chunks c+1, c+AD and c+PD-1 all exist (PD >= AD)
   int c0 = 0;
   for (; c0 + 2 * S::PD <= nchunks; c0 += S::PD) {
 #pragma unroll
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     const int c = c0 + p;
     if (c < nchunks)
       MOE_STREAM_CHUNK(p % S::PD, p & 1, p % S::AD, (p + 1) % S::AD, c, c + 1 < nchunks,
-                       c + S::AD < nchunks, c + S::PD < nchunks);
+                       c + S::AD < nchunks, c + S::PD - 1 < nchunks);
   }
 #undef MOE_STREAM_CHUNK
 

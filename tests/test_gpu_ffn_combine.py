@@ -128,7 +128,8 @@ def test_ffn_sampled_rows_full_size(cid, packed):
 @pytest.mark.parametrize("T,h,E,K,F,cf", [(1, 64, 1, 1, 64, 1.0), (300, 128, 5, 2, 192, 0.8),
                                           (1000, 256, 16, 2, 320, 1.0),
                                           (513, 64, 64, 6, 128, 1.0),
-                                          (2500, 192, 3, 1, 448, 1.5)])
+                                          (2500, 192, 3, 1, 448, 1.5),
+                                          (2048, 768, 14, 1, 3072, 1.0)])
 @pytest.mark.parametrize("packed", [False, True])
 def test_ffn_ragged_segments(T, h, E, K, F, cf, packed):
     banner(f"ffn ragged T={T} h={h} E={E} K={K} F={F} packed={packed}")
