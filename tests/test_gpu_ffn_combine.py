@@ -125,6 +125,25 @@ def test_ffn_sampled_rows_full_size(cid, packed):
     _check_rows(inp, sl, b, rows)
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_ffn_large_tiles_ragged(packed):
+    """Experts of ~3300 rows (not a multiple of the row tile) and F = 4096:
+    the MFMA-bound tiled kernel on ragged segments; sampled rows (each
+    expert's first and last, both sides of a 256-row boundary, random)."""
+    banner(f"ffn tiled ragged packed={packed}")
+    cfg = W.custom(T=16384, h=256, E=5, K=1, F=4096, cf=1.0, dtype="bf16", seed=31)
+    inp = custom_inputs(cfg)
+    _, _, cap, sl = _oracle_dispatch(inp)
+    b = _run_ffn(inp, cap, sl, packed)
+    offs = sl["expert_offsets"]
+    rng = np.random.default_rng(31)
+    rows = {int(r) for e in range(cfg.E) if offs[e + 1] > offs[e]
+            for r in (offs[e], offs[e + 1] - 1, offs[e] + 255, offs[e] + 256)
+            if offs[e] <= r < offs[e + 1]}
+    rows.update(rng.integers(0, sl["R"], 64).tolist())
+    _check_rows(inp, sl, b, np.array(sorted(rows)))
+
+
 @pytest.mark.parametrize("T,h,E,K,F,cf", [(1, 64, 1, 1, 64, 1.0), (300, 128, 5, 2, 192, 0.8),
                                           (1000, 256, 16, 2, 320, 1.0),
                                           (513, 64, 64, 6, 128, 1.0),
