@@ -75,15 +75,15 @@ size_t moe_workspace_bytes(const moe_cfg* cfg) {
   size_t a = dispatch_ws_bytes(A, cfg->E);
   size_t b = ledger_ws_bytes(A, cfg->E, kMaxRanks);
   size_t c = (size_t)kFp8AmaxBlocks * sizeof(uint32_t);  // moe_fp8_scale partials
+  size_t d = cfg->dtype == MOE_BF16 ? router_parts_bytes(cfg->T, cfg->h, cfg->E, cfg->K) : 0;
   size_t m = a > b ? a : b;
-  return (m > c ? m : c) + 256;
+  m = m > c ? m : c;
+  return (m > d ? m : d) + 256;
 }
 
 int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate, const float* logit_bias,
               float* logits, int32_t* topk_idx, float* topk_gate, int32_t* expert_load,
               void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   int st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -98,12 +98,9 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate, const float
   if (x) {
     if (cfg->dtype == MOE_BF16) {
       if (!aligned16(x) || !aligned16(w_gate)) return MOE_ERR_INVALID_ARG;
-      if (E <= 64 && K <= 16)
-        return hip_status(launch_router_topk_bf16((const uint16_t*)x, (const uint16_t*)w_gate,
-                                                  logit_bias, logits, topk_idx, topk_gate,
-                                                  expert_load, T, h, E, K, s));
-      st = hip_status(launch_router_gemm_bf16((const uint16_t*)x, (const uint16_t*)w_gate,
-                                              logits, T, h, E, s));
+      return hip_status(launch_router_bf16((const uint16_t*)x, (const uint16_t*)w_gate,
+                                           logit_bias, logits, topk_idx, topk_gate, expert_load,
+                                           T, h, E, K, ws, ws ? ws_bytes : 0, s));
     } else {
       st = hip_status(launch_router_gemm_f32((const float*)x, (const float*)w_gate, logits, T,
                                              h, E, s));

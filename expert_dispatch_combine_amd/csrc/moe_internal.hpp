@@ -66,8 +66,6 @@ inline size_t ledger_final_bytes(int E, int n_ep) {
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the first HIP error.
-hipError_t launch_router_gemm_bf16(const uint16_t* x, const uint16_t* wg, float* logits,
-                                   int T, int h, int E, hipStream_t s);
 // bias[e] += alpha * (mean - count[e]), count = histogram of topk_idx[:, 0]
 hipError_t launch_bias_update(const int32_t* idx, int T, int K, int E, float alpha, float* bias,
                               int32_t* counts, hipStream_t s);
@@ -76,6 +74,15 @@ hipError_t launch_router_topk_bf16(const uint16_t* x, const uint16_t* wg, const 
                                    int T, int h, int E, int K, hipStream_t s);
 hipError_t launch_router_gemm_f32(const float* x, const float* wg, float* logits, int T,
                                   int h, int E, hipStream_t s);
+// bf16 router, every batch shape: product + top-k + softmax (+ histogram).
+hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wg, const float* bias,
+                              float* logits, int32_t* idx, float* gate, int32_t* load, int T,
+                              int h, int E, int K, void* ws, size_t ws_bytes, hipStream_t s);
+// Workspace bytes launch_router_bf16 uses for split partial products (0: none).
+size_t router_parts_bytes(int T, int h, int E, int K);
+hipError_t launch_topk_parts(float* logits, const float* parts, int KS, const float* bias,
+                             int32_t* idx, float* gate, int32_t* load, int T, int E, int K,
+                             hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 hipError_t launch_topk_softmax(const float* logits, const float* bias, int32_t* idx,
                                float* gate, int32_t* load, int T, int E, int K,

@@ -119,3 +119,70 @@ def test_router_product_ragged_shapes(T, h, E, K):
     tie = near_tie_tokens(logits_o, None, K)
     same = np.all(b.topk_idx.cpu().numpy() == idx_o, axis=1)
     assert np.all(same | tie)
+
+
+@pytest.mark.parametrize("T,h,E,K,ws", [
+    (16390, 128, 64, 6, True),     # 64-token x 64-expert tiles, fused top-k, ragged T
+    (16400, 64, 20, 2, True),      # 128 x 32 tiles, E not a multiple of 4
+    (300, 512, 32, 20, True),      # K > 16: tiled product, 8 h ranges, separate top-k
+    (257, 1024, 256, 8, True),     # 64 x 256 tiles, 8 h ranges summed by the top-k
+    (257, 1024, 256, 8, False),    # same without workspace: one h range
+    (130, 192, 1001, 4, True),     # four expert tiles, odd E, h not splittable
+    (1000, 448, 130, 3, True),     # E just above one 128-expert tile
+    (90, 256, 100, 5, True),       # 64 x 128 tiles, 4 h ranges
+])
+def test_router_tiled_shapes(T, h, E, K, ws):
+    """The tiled router product (long batches or E > 64) on shapes that
+    exercise each tile shape, the h split with its partial sums, ragged token
+    and expert tiles, and the fused and separate top-k; the bias and the
+    expert histogram ride along."""
+    banner(f"route tiled T={T} h={h} E={E} K={K} ws={ws}")
+    cfg = W.custom(T=T, h=h, E=E, K=K, F=64, dtype="bf16", seed=T * 7 + E)
+    inp = custom_inputs(cfg, with_experts=False)
+    x64, wg64 = host(inp.x), host(inp.w_gate)
+    rng = np.random.default_rng(E + K)
+    bias = (rng.standard_normal(E) * 0.01).astype(np.float32)
+    b = buffers_for(cfg)
+    b.logits.fill_(float("nan"))
+    M.moe_route(b.cfg, inp.x, inp.w_gate, to_dev(bias, torch.float32), b.logits, b.topk_idx,
+                b.topk_gate, b.expert_load, b.ws if ws else None)
+    torch.cuda.synchronize()
+    lg = b.logits.cpu().numpy().astype(np.float64)
+    ref = x64 @ wg64.T
+    err = np.abs(lg - ref)
+    assert np.all(err <= logit_bound(x64, wg64) + 1e-30), float(np.nanmax(err))
+    logits_o = O.router_logits(x64, wg64)
+    idx_o, gate_o = O.topk_softmax(logits_o, K, bias)
+    idx_g = b.topk_idx.cpu().numpy()
+    gate_g = b.topk_gate.cpu().numpy()
+    tie = near_tie_tokens(logits_o, bias, K)
+    same = np.all(idx_g == idx_o, axis=1)
+    assert np.all(same | tie), np.nonzero(~(same | tie))[0][:10]
+    assert tie.mean() < 0.05
+    m = same & ~tie
+    tol = 2.0 * float(err.max()) + 2 * GATE_RTOL
+    np.testing.assert_allclose(gate_g[m], gate_o[m], rtol=tol, atol=1e-30)
+    # every token's ids are distinct and in range; the histogram is of the GPU's ids
+    assert idx_g.min() >= 0 and idx_g.max() < E
+    assert np.all(np.sort(idx_g, axis=1)[:, 1:] != np.sort(idx_g, axis=1)[:, :-1])
+    assert np.array_equal(b.expert_load.cpu().numpy().astype(np.int64),
+                          np.bincount(idx_g.reshape(-1), minlength=E))
+
+
+def test_router_tiled_is_deterministic():
+    """Two calls on the same inputs give the same bits (fixed summation order
+    of the h ranges; no atomics on values)."""
+    banner("route tiled determinism")
+    cfg = W.custom(T=1024, h=1024, E=256, K=8, F=64, dtype="bf16", seed=5)
+    inp = custom_inputs(cfg, with_experts=False)
+    outs = []
+    for _ in range(2):
+        b = buffers_for(cfg)
+        M.moe_route(b.cfg, inp.x, inp.w_gate, None, b.logits, b.topk_idx, b.topk_gate, None,
+                    b.ws)
+        torch.cuda.synchronize()
+        outs.append((b.logits.cpu().numpy().copy(), b.topk_idx.cpu().numpy().copy(),
+                     b.topk_gate.cpu().numpy().copy()))
+    for a, c in zip(outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              c.view(np.uint32) if c.dtype == np.float32 else c)
