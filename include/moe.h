@@ -128,7 +128,10 @@ size_t moe_workspace_bytes(const moe_cfg* cfg);
  *   topk_idx   [T, K]  int32      expert ids, slot 0 = largest
  *   topk_gate  [T, K]  fp32       softmax weights, each row sums to 1
  *   expert_load [E]    int32|NULL pre-capacity histogram of topk_idx
- * The workspace is not used today (may be NULL). */
+ * ws (16-byte aligned, may be NULL): for long batches or many experts the
+ * bf16 product splits h into ranges whose fp32 partial products are kept
+ * there and added in range order; with no (or too small a) workspace the
+ * product runs unsplit, slower but equally valid.  Logits are not NaN. */
 int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate,
               const float* logit_bias, float* logits, int32_t* topk_idx,
               float* topk_gate, int32_t* expert_load, void* ws, size_t ws_bytes,
