@@ -21,7 +21,7 @@
 //    one linear stream, which is what HBM serves at full rate (row-major
 //    fragments touch 32 rows x 32 bytes per load and run ~30% slower).
 //
-// Two kernel shapes, chosen per launch on the host:
+// Three kernel shapes, chosen per launch on the host:
 //  * streaming (rows per expert up to a few hundred: weight-bandwidth bound).
 //    A workgroup takes ALL rows of one expert (up to 160, in 32-row MFMA
 //    tiles) and 32*WN weight rows, so each weight byte crosses HBM once.
@@ -34,6 +34,10 @@
 //    fixed order.
 //  * tiled (hundreds of rows per expert: MFMA bound).  128 x BN tiles with
 //    both operands double-buffered in LDS, 4 waves in a 2 x 2 grid.
+//  * wide (over ~500 rows per expert and a weight dim divisible by 256):
+//    256 x 256 tiles, each wave 128 x 128, which halves the LDS fragment
+//    reads per MFMA; global loads two chunks ahead, issued and staged a
+//    quarter per k-step between the MFMAs.
 //
 // Scheduling is on the device (no host sync): every workgroup derives the
 // per-expert tile counts from `offsets`, maps its id to a logical tile with an
@@ -538,6 +542,184 @@ __global__ __launch_bounds__(256, 2) void tiled_gemm_kernel(
 }
 
 // ==========================================================================
+// wide tiled kernel: 256 activation rows x BN weight rows per workgroup
+// ==========================================================================
+// Each of the 4 waves (2 x 2) owns 128 rows x BN/2 columns, i.e. 4 x BN/64
+// MFMA tiles, so a 16-wide k-step costs 4 + BN/64 fragment reads from LDS for
+// 4 * BN/64 MFMAs (half the LDS traffic per MFMA of the 128 x 128 tiling).
+// Both operands are staged through XOR-swizzled, double-buffered LDS tiles
+// (64 k per stage); the global loads run two chunks ahead in registers and
+// the LDS fragment reads one k-step ahead of their MFMAs.  Loads and LDS
+// staging are spread over the four k-steps: issued in one burst they held
+// each chunk's first step up by several hundred ns.  One workgroup per CU
+// (the accumulators fill the AGPRs).
+constexpr int WBM = 256;
+
+template <int BN, int EPI, bool PK>
+__global__ __launch_bounds__(256, 1) void wide_gemm_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+    const float* __restrict__ bias, void* __restrict__ out,
+    const int32_t* __restrict__ offsets, int E, int N, int Kd) {
+  constexpr int TM = 4;                // 32-row MFMA tiles per wave
+  constexpr int TN = BN / 64;          // 32-column MFMA tiles per wave
+  constexpr int AQ = WBM * 8 / 256;    // 16-byte quads per thread and chunk: activations
+  constexpr int WQ = BN * 8 / 256;     // weights
+  constexpr int NQ = AQ + WQ;
+  constexpr int ASTG = WBM * 64;       // bf16 elements of one activation stage
+  constexpr int STG = ASTG + BN * 64;  // one stage: activations, then weights
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STG];
+  __shared__ TileInfo tinfo;
+
+  const int tid = threadIdx.x;
+  if (!find_tile<WBM, BN>(offsets, E, N, &tinfo, tid)) return;
+  const int e = tinfo.e, row0 = tinfo.row0, row_end = tinfo.row_end, n0 = tinfo.n0;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int li = lane & 31, lg = lane >> 5;
+  const int nk = Kd / 64;
+
+  // staging: quad j of this thread is row (tid / 8) + 32 j, quad tid % 8 of
+  // the chunk (packed weights: quad tid of the 4 KB block of strip j, copied
+  // linearly).  Sources are 32-bit element offsets from per-tile bases;
+  // chunk c adds c * 64 (activations, row-major weights) or c * PBLK.  The
+  // swizzle of row r + 32 j equals that of r, so LDS slots step by 32 rows.
+  const uint16_t* abase = A + (size_t)row0 * Kd;
+  const uint16_t* wbase = PK ? W + ((size_t)e * (N / 32) + n0 / 32) * nk * PBLK
+                             : W + ((size_t)e * N + n0) * Kd;
+  const int sr = tid >> 3, sq = tid & 7;
+  // (unsigned, so that the loads take a scalar base plus a 32-bit offset)
+  uint32_t aoff[AQ];
+#pragma unroll
+  for (int j = 0; j < AQ; ++j)
+    aoff[j] = (uint32_t)((min(row0 + sr + 32 * j, row_end - 1) - row0) * Kd + sq * 8);
+  const uint32_t woff0 = PK ? tid * 8 : sr * Kd + sq * 8;
+  const uint32_t wjstr = PK ? nk * PBLK : 32 * Kd;  // next quad of this thread
+  const int adst = act_slot(sr, sq);
+  const int wdst = PK ? ASTG + tid * 8 : ASTG + act_slot(sr, sq);
+  constexpr int WDJ = PK ? PBLK : 32 * 64;     // LDS step of the next quad
+  constexpr int WCSTR = PK ? PBLK : 64;
+
+  // fragments at k-step 0; step s XORs (s << 3) (packed: k = 32 lg + 8 s)
+  // or (2 s << 3) (row-major: k = 16 s + 8 lg) into the slot
+  int afr[TM], wfr[TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) afr[tm] = act_slot(wm * 128 + tm * 32 + li, PK ? 4 * lg : lg);
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn)
+    wfr[tn] = PK ? ASTG + (wn * TN + tn) * PBLK + lane * 8
+                 : ASTG + act_slot(wn * (BN / 2) + tn * 32 + li, lg);
+  constexpr int SSH = PK ? 3 : 4;          // slot XOR of step s: s << SSH
+  constexpr int WSTEP = PK ? 512 : 0;      // packed weights: step s adds s * 512
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
+
+  // global -> registers two chunks ahead; LDS fragments one k-step ahead
+  u32x4 reg[2][NQ];
+#define MOE_WIDE_LOAD(SLOT, c)                                                               \
+  do {                                                                                       \
+    _Pragma("unroll") for (int j = 0; j < AQ; ++j) reg[SLOT][j] =                            \
+        *(const u32x4*)(abase + (aoff[j] + (uint32_t)(c) * 64u));                            \
+    _Pragma("unroll") for (int j = 0; j < WQ; ++j) reg[SLOT][AQ + j] =                       \
+        *(const u32x4*)(wbase + (woff0 + j * wjstr + (uint32_t)(c) * WCSTR));                \
+  } while (0)
+#define MOE_WIDE_STORE(SLOT)                                                                 \
+  do {                                                                                       \
+    uint16_t* st_ = lds + (SLOT) * STG;                                                      \
+    _Pragma("unroll") for (int j = 0; j < AQ; ++j) *(u32x4*)(st_ + adst + j * 32 * 64) =     \
+        reg[SLOT][j];                                                                        \
+    _Pragma("unroll") for (int j = 0; j < WQ; ++j) *(u32x4*)(st_ + wdst + j * WDJ) =         \
+        reg[SLOT][AQ + j];                                                                   \
+  } while (0)
+#define MOE_WIDE_FRAGS(B, st_, s4)                                                           \
+  do {                                                                                       \
+    _Pragma("unroll") for (int tm = 0; tm < TM; ++tm) fa[B][tm] =                            \
+        *(const bf16x8*)((st_) + (afr[tm] ^ ((s4) << SSH)));                                 \
+    _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) fw[B][tn] =                            \
+        *(const bf16x8*)((st_) + (PK ? wfr[tn] + (s4) * WSTEP : (wfr[tn] ^ ((s4) << SSH)))); \
+  } while (0)
+  // chunk c (in LDS stage and register slot SLOT = c & 1), per k-step: a
+  // quarter of chunk c + 2's global loads into the slot, the next step's
+  // fragment reads, this step's MFMAs, then a quarter of chunk c + 1's quads
+  // into the other LDS buffer (nobody reads it until the barrier), so that
+  // load issue and staging overlap the MFMAs; the scheduling barriers keep
+  // that order.  In the steady-state loop REFILL and NEXT are compile-time
+  // true: without branches the compiler waits only for chunk c + 1's loads
+  // before staging them.
+  constexpr int QPS = NQ / 4;  // quads staged per k-step
+#define MOE_WIDE_CHUNK(SLOT, c, REFILL, NEXT)                                                \
+  do {                                                                                       \
+    const uint16_t* st = lds + (SLOT) * STG;                                                 \
+    uint16_t* nst = lds + ((SLOT) ^ 1) * STG;                                                \
+    MOE_WIDE_FRAGS(0, st, 0);                                                                \
+    _Pragma("unroll") for (int s4 = 0; s4 < 4; ++s4) {                                       \
+      if (REFILL) {                                                                          \
+        _Pragma("unroll") for (int jj = 0; jj < QPS; ++jj) {                                 \
+          const int j = s4 * QPS + jj;                                                       \
+          if (j < AQ)                                                                        \
+            reg[SLOT][j] = *(const u32x4*)(abase + (aoff[j] + (uint32_t)((c) + 2) * 64u));   \
+          else                                                                               \
+            reg[SLOT][j] = *(const u32x4*)(wbase + (woff0 + (j - AQ) * wjstr +               \
+                                                    (uint32_t)((c) + 2) * WCSTR));           \
+        }                                                                                    \
+      }                                                                                      \
+      if (s4 < 3) MOE_WIDE_FRAGS((s4 + 1) & 1, st, s4 + 1);                                 \
+      __builtin_amdgcn_sched_barrier(0);                                                     \
+      _Pragma("unroll") for (int tm = 0; tm < TM; ++tm)                                      \
+        _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) acc[tm][tn] =                      \
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s4 & 1][tn], fa[s4 & 1][tm],          \
+                                                    acc[tm][tn], 0, 0, 0);                   \
+      if (NEXT) {                                                                            \
+        _Pragma("unroll") for (int jj = 0; jj < QPS; ++jj) {                                 \
+          const int j = s4 * QPS + jj;                                                       \
+          if (j < AQ)                                                                        \
+            *(u32x4*)(nst + adst + j * 32 * 64) = reg[(SLOT) ^ 1][j];                        \
+          else                                                                               \
+            *(u32x4*)(nst + wdst + (j - AQ) * WDJ) = reg[(SLOT) ^ 1][j];                     \
+        }                                                                                    \
+      }                                                                                      \
+      __builtin_amdgcn_sched_barrier(0);                                                     \
+    }                                                                                        \
+    __syncthreads();                                                                         \
+  } while (0)
+  bf16x8 fa[2][TM], fw[2][TN];
+  MOE_WIDE_LOAD(0, 0);
+  if (nk > 1) MOE_WIDE_LOAD(1, 1);
+  MOE_WIDE_STORE(0);
+  __syncthreads();
+  int c0 = 0;
+  for (; c0 + 4 <= nk; c0 += 2) {
+    MOE_WIDE_CHUNK(0, c0, true, true);
+    MOE_WIDE_CHUNK(1, c0 + 1, true, true);
+  }
+  // tail: the last two or three chunks (c0 is even)
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int c = c0 + p;
+    if (c < nk) MOE_WIDE_CHUNK(p & 1, c, c + 2 < nk, c + 1 < nk);
+  }
+#undef MOE_WIDE_CHUNK
+#undef MOE_WIDE_LOAD
+#undef MOE_WIDE_STORE
+#undef MOE_WIDE_FRAGS
+
+  const float* bptr = bias + (size_t)e * N;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int m = row0 + wm * 128 + tm * 32 + li;
+    if (m >= row_end) continue;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+      store_tile<EPI>(acc[tm][tn], bptr, out, m, n0 + wn * (BN / 2) + tn * 32 + lg * 4, N);
+  }
+}
+
+// ==========================================================================
 // weight packing: row-major [E, N, K] -> fragment blocks (see file header)
 // ==========================================================================
 __global__ __launch_bounds__(256) void pack_weights_kernel(const u32x4* __restrict__ src,
@@ -638,6 +820,16 @@ hipError_t launch_stream_mt(int wn, bool occ1, const uint16_t* A, const uint16_t
 }
 
 template <int BN, int EPI, bool PK>
+hipError_t launch_wide(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
+                       const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
+                       hipStream_t s) {
+  const int64_t grid = grid_for(r_max, WBM, E, N, BN);
+  hipLaunchKernelGGL((wide_gemm_kernel<BN, EPI, PK>), dim3((unsigned)grid), dim3(256), 0, s, A,
+                     W, bias, out, offsets, E, N, Kd);
+  return hipGetLastError();
+}
+
+template <int BN, int EPI, bool PK>
 hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
                         const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
                         hipStream_t s) {
@@ -649,6 +841,8 @@ hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const float* bias,
 
 // Shape choice.  rows_typ = the rows a typical expert holds, min(capacity,
 // ceil(A/E)); rows_max = min(capacity, A) bounds every expert.
+//  - rows_typ >= 512 and N % 256 == 0: MFMA bound, long segments -> wide
+//    256 x 256 kernel (256-row tiles waste little of a segment).
 //  - rows_typ >= 384: the product is MFMA bound -> tiled 128 x BN kernel.
 //  - else streaming, with the row tile covering every expert's rows when
 //    rows_max <= 160 (each weight byte read once), else 128-row tiles; the
@@ -659,6 +853,8 @@ hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* b
                             void* out, const int32_t* offsets, int E, int N, int Kd,
                             int64_t r_max, int64_t rows_typ, int64_t rows_max,
                             hipStream_t s) {
+  if (rows_typ >= 512 && N % 256 == 0)
+    return launch_wide<256, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
   if (rows_typ >= 384) {
     const int64_t est = (r_max / TBM) * (N / 128);
     if (N % 128 == 0 && est >= 512)
