@@ -25,12 +25,61 @@ __device__ __forceinline__ void better(float& v, int& e, float v2, int e2) {
   }
 }
 
+// Value of a partner lane in the same 16-lane row, by DPP (no LDS round trip):
+// step 0 pairs lane ^ 1, step 1 lane ^ 2 (quad permutes), step 2 mirrors each
+// 8-lane half, step 3 each 16-lane row.  For a group of G <= 16 aligned lanes,
+// steps 0 .. log2(G) - 1 in this order combine every lane with the group.
+template <int STEP>
+__device__ __forceinline__ int dpp_partner(int v) {
+  constexpr int ctrl = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
+  return __builtin_amdgcn_mov_dpp(v, ctrl, 0xF, 0xF, false);
+}
+template <int STEP>
+__device__ __forceinline__ float dpp_partner(float v) {
+  return __int_as_float(dpp_partner<STEP>(__float_as_int(v)));
+}
+
+// (value, id) of the group's best lane in every lane of the group
+template <int G>
+__device__ __forceinline__ void group_best(float& bv, int& be) {
+  if constexpr (G <= 16) {
+    if constexpr (G >= 2) better(bv, be, dpp_partner<0>(bv), dpp_partner<0>(be));
+    if constexpr (G >= 4) better(bv, be, dpp_partner<1>(bv), dpp_partner<1>(be));
+    if constexpr (G >= 8) better(bv, be, dpp_partner<2>(bv), dpp_partner<2>(be));
+    if constexpr (G >= 16) better(bv, be, dpp_partner<3>(bv), dpp_partner<3>(be));
+  } else {
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, G);
+      const int oe = __shfl_xor(be, off, G);
+      better(bv, be, ov, oe);
+    }
+  }
+}
+
+// sum over the group in every lane of the group
+template <int G>
+__device__ __forceinline__ float group_sum(float s) {
+  if constexpr (G <= 16) {
+    if constexpr (G >= 2) s += dpp_partner<0>(s);
+    if constexpr (G >= 4) s += dpp_partner<1>(s);
+    if constexpr (G >= 8) s += dpp_partner<2>(s);
+    if constexpr (G >= 16) s += dpp_partner<3>(s);
+  } else {
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, G);
+  }
+  return s;
+}
+
+// vmax receives the largest value (slot 0's, known to every lane).
 template <int G, int VMAX>
 __device__ __forceinline__ void topk_group(const float (&val)[VMAX], int E, int K, int gl,
-                                           float& slot_v, int& slot_e) {
+                                           float& slot_v, int& slot_e, float& vmax) {
   uint32_t taken = 0;
   slot_v = -INFINITY;
   slot_e = 0x7fffffff;
+  vmax = -INFINITY;
   for (int k = 0; k < K; ++k) {
     float bv = -INFINITY;
     int be = 0x7fffffff;
@@ -39,13 +88,9 @@ __device__ __forceinline__ void topk_group(const float (&val)[VMAX], int E, int 
       const int e = gl + j * G;
       if (e < E && !((taken >> j) & 1u)) better(bv, be, val[j], e);
     }
-#pragma unroll
-    for (int off = G / 2; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, G);
-      const int oe = __shfl_xor(be, off, G);
-      better(bv, be, ov, oe);
-    }
+    group_best<G>(bv, be);
     // every lane of the group now holds the winner
+    if (k == 0) vmax = bv;
     if (be % G == gl && be < E) taken |= 1u << (be / G);
     if (gl == k) {
       slot_v = bv;
@@ -57,13 +102,9 @@ __device__ __forceinline__ void topk_group(const float (&val)[VMAX], int E, int 
 // Softmax over the K slots held by lanes 0..K-1 of a G-lane group (G >= K is
 // guaranteed by the launcher: groups are at least K lanes wide).
 template <int G>
-__device__ __forceinline__ float topk_gate(float slot_v, int gl, int K) {
-  const float vmax = __shfl(slot_v, 0, G);
+__device__ __forceinline__ float topk_gate(float slot_v, float vmax, int gl, int K) {
   const float w = (gl < K) ? expf(slot_v - vmax) : 0.0f;
-  float s = w;
-#pragma unroll
-  for (int off = G / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, G);
-  return w / s;
+  return w / group_sum<G>(w);
 }
 
 // --------------------------------------------------------------------------
@@ -113,8 +154,9 @@ __global__ __launch_bounds__(256) void topk_kernel(float* __restrict__ logits,
     }
     float sv;
     int se;
-    topk_group<G, VMAX>(val, E, K, gl, sv, se);
-    const float g = topk_gate<G>(sv, gl, K);
+    float vm;
+    topk_group<G, VMAX>(val, E, K, gl, sv, se, vm);
+    const float g = topk_gate<G>(sv, vm, gl, K);
     if (gl < K) {
       idx[(size_t)t * K + gl] = se;
       gate[(size_t)t * K + gl] = g;
@@ -350,8 +392,9 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   }
   float sv;
   int se;
-  topk_group<G, VMAX>(val, E, K, gl, sv, se);
-  const float g = topk_gate<G>(sv, gl, K);
+  float vm;
+  topk_group<G, VMAX>(val, E, K, gl, sv, se, vm);
+  const float g = topk_gate<G>(sv, vm, gl, K);
   if (t < T && gl < K) {
     idx[(size_t)t * K + gl] = se;
     gate[(size_t)t * K + gl] = g;
@@ -396,6 +439,43 @@ struct RouterTile {
 
 // quad q of LDS row r (64 bf16 per row) lives at quad q ^ ((r >> 1) & 7)
 __device__ __forceinline__ int rt_slot(int r, int q) { return r * 64 + ((q ^ ((r >> 1) & 7)) << 3); }
+
+// Top-k + softmax of the TT tokens of a logits tile in LDS ([TT][PITCH]),
+// G lanes per token, 256 / G tokens per pass.  hist: LDS expert histogram or
+// NULL.
+template <int G, int TT, int EE, int PITCH>
+__device__ __forceinline__ void tile_topk(const float* tile, const float* __restrict__ bias,
+                                          int32_t* __restrict__ idx, float* __restrict__ gate,
+                                          int* hist, int t0, int T, int E, int K) {
+  constexpr int VMAX = EE / G;
+  static_assert(VMAX <= 32, "one bit per slot of the taken mask");
+  const int tid = threadIdx.x;
+  const int gl = tid % G;
+  for (int p = 0; p < TT / (256 / G); ++p) {
+    const int tl = p * (256 / G) + tid / G;
+    const int t = t0 + tl;
+    float val[VMAX];
+#pragma unroll
+    for (int j = 0; j < VMAX; ++j) {
+      const int e = gl + j * G;
+      float v = -INFINITY;
+      if (e < E) {
+        v = tile[tl * PITCH + e];
+        if (bias) v = v + bias[e];
+      }
+      val[j] = v;
+    }
+    float sv, vm;
+    int se;
+    topk_group<G, VMAX>(val, E, K, gl, sv, se, vm);
+    const float g = topk_gate<G>(sv, vm, gl, K);
+    if (t < T && gl < K) {
+      idx[(size_t)t * K + gl] = se;
+      gate[(size_t)t * K + gl] = g;
+      if (hist) atomicAdd(&hist[se], 1);
+    }
+  }
+}
 
 template <int TT, int EE, int GT>
 __global__ __launch_bounds__(256) void router_tiled_kernel(
@@ -541,33 +621,20 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(
     const int tl = i / E, e = i - tl * E;
     if (t0 + tl < T) logits[(size_t)(t0 + tl) * E + e] = tile[tl * S::PITCH + e];
   }
-  constexpr int G = 16;
-  constexpr int VMAX = EE / G;
-  const int gl = tid % G;
-  for (int p = 0; p < TT / 16; ++p) {
-    const int tl = p * 16 + tid / G;
-    const int t = t0 + tl;
-    float val[VMAX];
-#pragma unroll
-    for (int j = 0; j < VMAX; ++j) {
-      const int e = gl + j * G;
-      float v = -INFINITY;
-      if (e < E) {
-        v = tile[tl * S::PITCH + e];
-        if (bias) v = v + bias[e];
-      }
-      val[j] = v;
+  // the narrowest lane group that holds K slots (fewer passes over the tile)
+  int* hp = load ? hist : nullptr;
+  bool done = false;
+  if constexpr (EE / 4 <= 32)
+    if (K <= 4) {
+      tile_topk<4, TT, EE, S::PITCH>(tile, bias, idx, gate, hp, t0, T, E, K);
+      done = true;
     }
-    float sv;
-    int se;
-    topk_group<G, VMAX>(val, E, K, gl, sv, se);
-    const float g = topk_gate<G>(sv, gl, K);
-    if (t < T && gl < K) {
-      idx[(size_t)t * K + gl] = se;
-      gate[(size_t)t * K + gl] = g;
-      if (load) atomicAdd(&hist[se], 1);
+  if constexpr (EE / 8 <= 32)
+    if (!done && K <= 8) {
+      tile_topk<8, TT, EE, S::PITCH>(tile, bias, idx, gate, hp, t0, T, E, K);
+      done = true;
     }
-  }
+  if (!done) tile_topk<16, TT, EE, S::PITCH>(tile, bias, idx, gate, hp, t0, T, E, K);
   if (load) {
     __syncthreads();
     for (int e = tid; e < E; e += 256)

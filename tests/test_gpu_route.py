@@ -123,6 +123,8 @@ def test_router_product_ragged_shapes(T, h, E, K):
 
 @pytest.mark.parametrize("T,h,E,K,ws", [
     (16390, 128, 64, 6, True),     # 64-token x 64-expert tiles, fused top-k, ragged T
+    (16400, 128, 50, 3, True),     # fused top-k on 4-lane groups (K <= 4)
+    (16500, 64, 48, 12, True),     # fused top-k on 16-lane groups (8 < K <= 16)
     (16400, 64, 20, 2, True),      # 128 x 32 tiles, E not a multiple of 4
     (300, 512, 32, 20, True),      # K > 16: tiled product, 8 h ranges, separate top-k
     (257, 1024, 256, 8, True),     # 64 x 256 tiles, 8 h ranges summed by the top-k
