@@ -150,7 +150,9 @@ def test_ffn_large_tiles_ragged(packed):
                                           (2500, 192, 3, 1, 448, 1.5),
                                           (2048, 768, 14, 1, 3072, 1.0),
                                           (3000, 128, 4, 1, 384, 1.3),
-                                          (2200, 256, 3, 1, 512, 1.0)])
+                                          (2200, 256, 3, 1, 512, 1.0),
+                                          (3000, 64, 4, 1, 256, 1.3),
+                                          (2600, 192, 4, 1, 256, 1.3)])
 @pytest.mark.parametrize("packed", [False, True])
 def test_ffn_ragged_segments(T, h, E, K, F, cf, packed):
     banner(f"ffn ragged T={T} h={h} E={E} K={K} F={F} packed={packed}")
