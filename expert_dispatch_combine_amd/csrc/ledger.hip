@@ -154,15 +154,11 @@ __global__ __launch_bounds__(256) void ledger_partial_kernel(
       }
     }
   }
-  // wave sums of the scalar counters, then one LDS atomic per wave
+  // wave sums of the scalar counters (DPP within rows, then the four rows),
+  // then one LDS atomic per wave
   int vals[7] = {c_lall, c_call, c_lacc, c_cacc, c_acc, c_bad_id, c_bad_rank};
 #pragma unroll
-  for (int q = 0; q < 7; ++q) {
-    int v = vals[q];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    vals[q] = v;
-  }
+  for (int q = 0; q < 7; ++q) vals[q] = wave_sum(vals[q]);
   if ((tid & 63) == 0) {
     atomicAdd(&s_cnt[LC_LOCAL_ALL], vals[0]);
     atomicAdd(&s_cnt[LC_CROSS_ALL], vals[1]);

@@ -88,6 +88,30 @@ hipError_t launch_topk_softmax(const float* logits, const float* bias, int32_t* 
                                float* gate, int32_t* load, int T, int E, int K,
                                hipStream_t s);
 
+// ---- cross-lane exchanges by DPP (no LDS round trip)
+// Value of a partner lane in the same 16-lane row: step 0 pairs lane ^ 1,
+// step 1 lane ^ 2 (quad permutes), step 2 mirrors each 8-lane half, step 3
+// each 16-lane row.  For a group of G <= 16 aligned lanes, steps 0 ..
+// log2(G) - 1 in this order combine every lane with the whole group.
+template <int STEP>
+__device__ __forceinline__ int dpp_partner(int v) {
+  constexpr int ctrl = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
+  return __builtin_amdgcn_mov_dpp(v, ctrl, 0xF, 0xF, false);
+}
+template <int STEP>
+__device__ __forceinline__ float dpp_partner(float v) {
+  return __int_as_float(dpp_partner<STEP>(__float_as_int(v)));
+}
+// sum over the 64 lanes of a wave (every lane active), returned to all lanes
+__device__ __forceinline__ int wave_sum(int v) {
+  v += dpp_partner<0>(v);
+  v += dpp_partner<1>(v);
+  v += dpp_partner<2>(v);
+  v += dpp_partner<3>(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
 // ---- OCP E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
 // infinities; 0x7F/0xFF = NaN; largest finite 448), as in "MoE大模型专家并行与
 // 动态路由优化" 4.3 (FP8 all-to-all payload).

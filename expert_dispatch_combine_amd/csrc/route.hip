@@ -25,21 +25,8 @@ __device__ __forceinline__ void better(float& v, int& e, float v2, int e2) {
   }
 }
 
-// Value of a partner lane in the same 16-lane row, by DPP (no LDS round trip):
-// step 0 pairs lane ^ 1, step 1 lane ^ 2 (quad permutes), step 2 mirrors each
-// 8-lane half, step 3 each 16-lane row.  For a group of G <= 16 aligned lanes,
-// steps 0 .. log2(G) - 1 in this order combine every lane with the group.
-template <int STEP>
-__device__ __forceinline__ int dpp_partner(int v) {
-  constexpr int ctrl = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
-  return __builtin_amdgcn_mov_dpp(v, ctrl, 0xF, 0xF, false);
-}
-template <int STEP>
-__device__ __forceinline__ float dpp_partner(float v) {
-  return __int_as_float(dpp_partner<STEP>(__float_as_int(v)));
-}
-
-// (value, id) of the group's best lane in every lane of the group
+// (value, id) of the group's best lane in every lane of the group (groups of
+// up to 16 lanes exchange by DPP, see dpp_partner)
 template <int G>
 __device__ __forceinline__ void group_best(float& bv, int& be) {
   if constexpr (G <= 16) {
