@@ -51,12 +51,7 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
 __device__ __forceinline__ int block_exclusive_scan(int v, int* sh_wave, int tid) {
   // 256 threads = 4 waves
   const int lane = tid & 63, wave = tid >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
+  const int incl = wave_incl_scan(v);
   if (lane == 63) sh_wave[wave] = incl;
   __syncthreads();
   int prefix = 0;

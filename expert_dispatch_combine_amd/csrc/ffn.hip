@@ -97,13 +97,8 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
       const int rows = offsets[e + 1] - offsets[e];
       mine += (rows + BM - 1) / BM * ntn;
     }
-    int incl = mine;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
-    const int total = __shfl(incl, 63, 64);
+    const int incl = wave_incl_scan(mine);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
     const int per_xcd = (total + NXCD - 1) / NXCD;
     const int bid = blockIdx.x;
     int L = -1;

@@ -102,6 +102,21 @@ template <int STEP>
 __device__ __forceinline__ float dpp_partner(float v) {
   return __int_as_float(dpp_partner<STEP>(__float_as_int(v)));
 }
+// inclusive prefix sum over the 64 lanes of a wave (every lane active): a
+// shift-and-add scan inside each 16-lane row (lanes shifted in from outside
+// the row read 0), then the totals of the lower rows
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (int)(threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 // sum over the 64 lanes of a wave (every lane active), returned to all lanes
 __device__ __forceinline__ int wave_sum(int v) {
   v += dpp_partner<0>(v);
