@@ -194,7 +194,11 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     const int32_t* __restrict__ offsets, int E, int N, int Kd) {
   using S = StreamShape<MT, WN, WK, OCC>;
   static_assert(S::PD % S::AD == 0 && S::PD % 2 == 0, "ring sizes");
-  __shared__ __attribute__((aligned(16))) char lds[S::LDS_BYTES];
+  // the epilogue stages all BM output rows at once when they fit in 48 KB
+  constexpr int OUT_ALL = MT * 32 * (S::BN * (EPI == 0 ? 2 : 4) + 16);
+  constexpr bool ONE_PASS = OUT_ALL <= 48 * 1024;
+  constexpr int LDS_SZ = ONE_PASS && OUT_ALL > S::LDS_BYTES ? OUT_ALL : S::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) char lds[LDS_SZ];
   __shared__ TileInfo tinfo;
   uint16_t* act = (uint16_t*)lds;  // [2][BM rows][8 quads], swizzled
 
@@ -371,6 +375,37 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     for (int q = 0; q < 4; ++q) bq[q] = *(const float4*)(bptr + q * 8);
   }
   char* tile = lds;
+  if constexpr (ONE_PASS) {
+    __syncthreads();  // LDS free: k-loop / reduction done
+    if (kw == 0) {
+#pragma unroll
+      for (int tm = 0; tm < MT; ++tm) {
+        if (row0 + tm * 32 >= row_end) break;  // uniform
+        char* rowp = tile + (tm * 32 + li) * ROWB + (wn * 32 + lg * 4) * ESZ;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float v0 = acc[tm][4 * q + 0] + bq[q].x, v1 = acc[tm][4 * q + 1] + bq[q].y;
+          const float v2 = acc[tm][4 * q + 2] + bq[q].z, v3 = acc[tm][4 * q + 3] + bq[q].w;
+          if (EPI == 0) {
+            uint2 pk;
+            pk.x = pack_bf16x2(gelu_tanh_bf16(v0), gelu_tanh_bf16(v1));
+            pk.y = pack_bf16x2(gelu_tanh_bf16(v2), gelu_tanh_bf16(v3));
+            *(uint2*)(rowp + q * 8 * ESZ) = pk;
+          } else {
+            *(float4*)(rowp + q * 8 * ESZ) = make_float4(v0, v1, v2, v3);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int rows = min(S::BM, row_end - row0);
+    char* gout = (char*)out + ((size_t)row0 * N + n0) * ESZ;
+    for (int i = tid; i < rows * CPR; i += 256) {
+      const int r = i / CPR, c = i - r * CPR;
+      *(u32x4*)(gout + (size_t)r * N * ESZ + c * 16) = *(const u32x4*)(tile + r * ROWB + c * 16);
+    }
+    return;
+  }
 #pragma unroll
   for (int tm = 0; tm < MT; ++tm) {
     if (row0 + tm * 32 >= row_end) break;  // uniform
