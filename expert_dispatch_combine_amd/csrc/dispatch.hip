@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     const float* __restrict__ q_scale) {
   __shared__ int tot[kMaxExperts], bef[kMaxExperts], off[kMaxExperts + 1];
   __shared__ int sh_wave[4];
-  __shared__ int dst[SBR], src[SBR];
+  __shared__ int dst[SBR], src[SBR], own_id[SBR];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int base = blockIdx.x * SBR;
   for (int e = tid; e < E; e += 256) tot[e] = bef[e] = 0;
@@ -264,6 +264,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     for (int u = 0; u < 8; ++u) {
       const int i = i0 + u * 256 + tid;
       const int id = ids[u];
+      if (i >= base && i < base + SBR) own_id[i - base] = id;  // this block's routes
       const bool valid = id >= 0 && id < E;
       uint64_t m = __ballot(valid);
       for (int bit = 0; bit < nbits; ++bit) {
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     // rank = routes before the block + lanes below with the same expert
     const int i = base + lane;
     int id = -1;
-    if (lane < SBR && i < A) id = idx[i];
+    if (lane < SBR && i < A) id = own_id[lane];  // kept by the histogram pass
     const bool valid = lane < SBR && i < A && id >= 0 && id < E;
     uint64_t m = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
