@@ -756,7 +756,7 @@ RouterPlan router_plan(int T, int h, int E, int K, size_t parts_room) {
   if (E <= 32) { p.tt = 128; p.ee = 32; }
   else if (E <= 64) { p.tt = 64; p.ee = 64; }
   else if (E <= 128) { p.tt = 64; p.ee = 128; }
-  else { p.tt = 64; p.ee = 256; }
+  else { p.tt = 128; p.ee = 128; }  // several expert tiles: x is re-read per tile
   const int64_t tiles = (int64_t)((T + p.tt - 1) / p.tt) * ((E + p.ee - 1) / p.ee);
   // split h while the launch still fits one workgroup per CU (256 CUs)
   p.ks = 1;
@@ -811,12 +811,12 @@ hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* wg, const float
   else if (p.ee == 64)
     err = launch_router_tiled_t<64, 64, 2>(x, wg, bias, logits, parts, idx, gate, load, T, h,
                                            E, K, p.ks, p.fuse, s);
-  else if (p.ee == 128)
+  else if (p.tt == 64)
     err = launch_router_tiled_t<64, 128, 2>(x, wg, bias, logits, parts, idx, gate, load, T, h,
                                             E, K, p.ks, p.fuse, s);
   else
-    err = launch_router_tiled_t<64, 256, 1>(x, wg, bias, logits, parts, idx, gate, load, T, h,
-                                            E, K, p.ks, p.fuse, s);
+    err = launch_router_tiled_t<128, 128, 2>(x, wg, bias, logits, parts, idx, gate, load, T, h,
+                                             E, K, p.ks, p.fuse, s);
   if (err != hipSuccess || p.fuse) return err;
   return launch_topk_parts(logits, parts, p.ks, bias, idx, gate, load, T, E, K, s);
 }

@@ -127,9 +127,9 @@ def test_router_product_ragged_shapes(T, h, E, K):
     (16500, 64, 48, 12, True),     # fused top-k on 16-lane groups (8 < K <= 16)
     (16400, 64, 20, 2, True),      # 128 x 32 tiles, E not a multiple of 4
     (300, 512, 32, 20, True),      # K > 16: tiled product, 8 h ranges, separate top-k
-    (257, 1024, 256, 8, True),     # 64 x 256 tiles, 8 h ranges summed by the top-k
+    (257, 1024, 256, 8, True),     # 128 x 128 tiles, two expert tiles, 8 h ranges summed
     (257, 1024, 256, 8, False),    # same without workspace: one h range
-    (130, 192, 1001, 4, True),     # four expert tiles, odd E, h not splittable
+    (130, 192, 1001, 4, True),     # eight expert tiles, odd E, h not splittable
     (1000, 448, 130, 3, True),     # E just above one 128-expert tile
     (90, 256, 100, 5, True),       # 64 x 128 tiles, 4 h ranges
 ])
