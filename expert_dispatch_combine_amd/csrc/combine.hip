@@ -93,7 +93,29 @@ hipError_t launch_combine(const float* y, const int32_t* route_row, const float*
   if (TB > kMaxTB) TB = kMaxTB;
   if (TB < 1) TB = 1;
   const int grid = (T + TB - 1) / TB;
-  if (vec)
+  // one token per workgroup and rows of up to 2048 vectors: every thread
+  // takes all its vectors in one trip (no partly idle second trip)
+  const int u1 = (hv + 255) / 256;
+  if (vec && TB == 1 && u1 > U && u1 <= 8) {
+    switch (u1) {
+      case 5:
+        hipLaunchKernelGGL((combine_kernel<true, 5>), dim3(grid), dim3(256), 0, s, y,
+                           route_row, gate, out, T, K, h, TB);
+        break;
+      case 6:
+        hipLaunchKernelGGL((combine_kernel<true, 6>), dim3(grid), dim3(256), 0, s, y,
+                           route_row, gate, out, T, K, h, TB);
+        break;
+      case 7:
+        hipLaunchKernelGGL((combine_kernel<true, 7>), dim3(grid), dim3(256), 0, s, y,
+                           route_row, gate, out, T, K, h, TB);
+        break;
+      default:
+        hipLaunchKernelGGL((combine_kernel<true, 8>), dim3(grid), dim3(256), 0, s, y,
+                           route_row, gate, out, T, K, h, TB);
+        break;
+    }
+  } else if (vec)
     hipLaunchKernelGGL((combine_kernel<true, U>), dim3(grid), dim3(256), 0, s, y, route_row,
                        gate, out, T, K, h, TB);
   else

@@ -204,7 +204,9 @@ def _check_combine(T, K, h, R, drop_frac, seed):
 
 @pytest.mark.parametrize("T,K,h,R,drop", [(1, 1, 4, 1, 0.0), (64, 2, 32, 119, 0.1),
                                           (2048, 1, 768, 2048, 0.0), (300, 8, 100, 2000, 0.3),
-                                          (1000, 6, 2048, 3000, 0.5), (77, 3, 13, 50, 0.2)])
+                                          (1000, 6, 2048, 3000, 0.5), (77, 3, 13, 50, 0.2),
+                                          (40, 2, 4100, 60, 0.1), (33, 3, 6000, 80, 0.2),
+                                          (20, 8, 8192, 150, 0.0), (9, 4, 8196, 30, 0.3)])
 def test_combine(T, K, h, R, drop):
     banner(f"combine T={T} K={K} h={h}")
     _check_combine(T, K, h, R, drop, seed=T + h)
