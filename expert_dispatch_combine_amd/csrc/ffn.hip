@@ -32,12 +32,14 @@
 //    waves split each 64-wide k-chunk when the weight dim is too short to
 //    give the chip enough work; their partial sums are added in LDS in a
 //    fixed order.
-//  * tiled (hundreds of rows per expert: MFMA bound).  128 x BN tiles with
-//    both operands double-buffered in LDS, 4 waves in a 2 x 2 grid.
-//  * wide (over ~500 rows per expert and a weight dim divisible by 256):
-//    256 x 256 tiles, each wave 128 x 128, which halves the LDS fragment
-//    reads per MFMA; global loads two chunks ahead, issued and staged a
-//    quarter per k-step between the MFMAs.
+//  * tiled (hundreds of rows per expert, weight dim not a multiple of 128):
+//    128 x 64 tiles with both operands double-buffered in LDS, 4 waves in a
+//    2 x 2 grid.
+//  * wide (hundreds of rows per expert, MFMA bound): 256 x 256 tiles at one
+//    workgroup per CU (each wave 128 x 128, which halves the LDS fragment
+//    reads per MFMA of a 128 x 128 tiling) or 128 x 128 tiles at two per CU;
+//    global loads two chunks ahead, issued and staged a quarter per k-step
+//    between the MFMAs.
 //
 // Scheduling is on the device (no host sync): every workgroup derives the
 // per-expert tile counts from `offsets`, maps its id to a logical tile with an
@@ -572,25 +574,23 @@ __global__ __launch_bounds__(256, 2) void tiled_gemm_kernel(
 }
 
 // ==========================================================================
-// wide tiled kernel: 256 activation rows x BN weight rows per workgroup
+// wide tiled kernel: WBM activation rows x BN weight rows per workgroup
 // ==========================================================================
-// Each of the 4 waves (2 x 2) owns 128 rows x BN/2 columns, i.e. 4 x BN/64
-// MFMA tiles, so a 16-wide k-step costs 4 + BN/64 fragment reads from LDS for
-// 4 * BN/64 MFMAs (half the LDS traffic per MFMA of the 128 x 128 tiling).
+// Each of the 4 waves (2 x 2) owns WBM/2 rows x BN/2 columns, i.e. WBM/64 x
+// BN/64 MFMA tiles; with 256 x 256 a 16-wide k-step costs 8 fragment reads
+// from LDS for 16 MFMAs (half the LDS traffic per MFMA of 128 x 128).
 // Both operands are staged through XOR-swizzled, double-buffered LDS tiles
 // (64 k per stage); the global loads run two chunks ahead in registers and
 // the LDS fragment reads one k-step ahead of their MFMAs.  Loads and LDS
 // staging are spread over the four k-steps: issued in one burst they held
-// each chunk's first step up by several hundred ns.  One workgroup per CU
-// (the accumulators fill the AGPRs).
-constexpr int WBM = 256;
-
-template <int BN, int EPI, bool PK>
-__global__ __launch_bounds__(256, 1) void wide_gemm_kernel(
+// each chunk's first step up by several hundred ns.  256 x 256: one
+// workgroup per CU (the accumulators fill the AGPRs); 128 x 128: two.
+template <int WBM, int BN, int EPI, bool PK, int OCC>
+__global__ __launch_bounds__(256, OCC) void wide_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, void* __restrict__ out,
     const int32_t* __restrict__ offsets, int E, int N, int Kd) {
-  constexpr int TM = 4;                // 32-row MFMA tiles per wave
+  constexpr int TM = WBM / 64;         // 32-row MFMA tiles per wave
   constexpr int TN = BN / 64;          // 32-column MFMA tiles per wave
   constexpr int AQ = WBM * 8 / 256;    // 16-byte quads per thread and chunk: activations
   constexpr int WQ = BN * 8 / 256;     // weights
@@ -633,7 +633,8 @@ __global__ __launch_bounds__(256, 1) void wide_gemm_kernel(
   // or (2 s << 3) (row-major: k = 16 s + 8 lg) into the slot
   int afr[TM], wfr[TN];
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) afr[tm] = act_slot(wm * 128 + tm * 32 + li, PK ? 4 * lg : lg);
+  for (int tm = 0; tm < TM; ++tm)
+    afr[tm] = act_slot(wm * (WBM / 2) + tm * 32 + li, PK ? 4 * lg : lg);
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn)
     wfr[tn] = PK ? ASTG + (wn * TN + tn) * PBLK + lane * 8
@@ -741,7 +742,7 @@ __global__ __launch_bounds__(256, 1) void wide_gemm_kernel(
   const float* bptr = bias + (size_t)e * N;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
-    const int m = row0 + wm * 128 + tm * 32 + li;
+    const int m = row0 + wm * (WBM / 2) + tm * 32 + li;
     if (m >= row_end) continue;
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
@@ -849,13 +850,13 @@ hipError_t launch_stream_mt(int wn, bool occ1, const uint16_t* A, const uint16_t
   return hipErrorInvalidValue;
 }
 
-template <int BN, int EPI, bool PK>
+template <int WBM, int BN, int EPI, bool PK, int OCC>
 hipError_t launch_wide(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
                        const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
                        hipStream_t s) {
   const int64_t grid = grid_for(r_max, WBM, E, N, BN);
-  hipLaunchKernelGGL((wide_gemm_kernel<BN, EPI, PK>), dim3((unsigned)grid), dim3(256), 0, s, A,
-                     W, bias, out, offsets, E, N, Kd);
+  hipLaunchKernelGGL((wide_gemm_kernel<WBM, BN, EPI, PK, OCC>), dim3((unsigned)grid), dim3(256),
+                     0, s, A, W, bias, out, offsets, E, N, Kd);
   return hipGetLastError();
 }
 
@@ -871,9 +872,12 @@ hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const float* bias,
 
 // Shape choice.  rows_typ = the rows a typical expert holds, min(capacity,
 // ceil(A/E)); rows_max = min(capacity, A) bounds every expert.
-//  - rows_typ >= 512 and N % 256 == 0: MFMA bound, long segments -> wide
-//    256 x 256 kernel (256-row tiles waste little of a segment).
-//  - rows_typ >= 384: the product is MFMA bound -> tiled 128 x BN kernel.
+//  - rows_typ >= 512, N % 256 == 0, first GEMM (N = F, the long weight
+//    dim): MFMA bound, long segments -> wide kernel, 256 x 256 tiles.
+//  - rows_typ >= 384, N % 128 == 0: wide kernel, 128 x 128 tiles, two
+//    workgroups per CU (finer tiles quantise better over 256 CUs; for the
+//    second GEMM they were as fast or faster than 256 x 256).
+//  - rows_typ >= 384, other N (multiple of 64): tiled 128 x 64 kernel.
 //  - else streaming, with the row tile covering every expert's rows when
 //    rows_max <= 160 (each weight byte read once), else 128-row tiles; the
 //    weight-tile width 32*WN is the widest that still gives >= 256
@@ -883,14 +887,12 @@ hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* b
                             void* out, const int32_t* offsets, int E, int N, int Kd,
                             int64_t r_max, int64_t rows_typ, int64_t rows_max,
                             hipStream_t s) {
-  if (rows_typ >= 512 && N % 256 == 0)
-    return launch_wide<256, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
-  if (rows_typ >= 384) {
-    const int64_t est = (r_max / TBM) * (N / 128);
-    if (N % 128 == 0 && est >= 512)
-      return launch_tiled<128, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+  if (rows_typ >= 512 && N % 256 == 0 && EPI == 0)
+    return launch_wide<256, 256, EPI, PK, 1>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+  if (rows_typ >= 384 && N % 128 == 0)
+    return launch_wide<128, 128, EPI, PK, 2>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+  if (rows_typ >= 384)
     return launch_tiled<64, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
-  }
   int mt = (int)((rows_max + 31) / 32);
   if (mt > 5) mt = 4;
   if (mt < 1) mt = 1;
