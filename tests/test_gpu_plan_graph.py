@@ -28,7 +28,8 @@ def _same(a, c):
     assert a["acc"] == c["acc"] and a["P"] == c["P"] and a["loads"] == c["loads"]
 
 
-@pytest.mark.parametrize("cid,packed", [(1, False), (2, False), (2, True), (5, True)])
+@pytest.mark.parametrize("cid,packed", [(1, False), (2, False), (2, True), (3, True), (4, True),
+                                        (5, True)])
 def test_plan_and_graph_replay_match_eager(cid, packed):
     banner(f"plan/graph config {cid} packed={packed}")
     inp = device_inputs(cid)
