@@ -798,8 +798,20 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
   const int e = expert_of_row(offsets, E, row);
   const float* a = A + (size_t)row * Kd;
   const float* w = W + ((size_t)e * N + n) * Kd;
+  // sequential fp32 FMAs over k; the loads of 8 k go out before their FMAs
   float acc = 0.f;
-  for (int k = 0; k < Kd; ++k) acc = fmaf(a[k], w[k], acc);
+  int k = 0;
+  for (; k + 8 <= Kd; k += 8) {
+    float av[8], wv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      av[u] = a[k + u];
+      wv[u] = w[k + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = fmaf(av[u], wv[u], acc);
+  }
+  for (; k < Kd; ++k) acc = fmaf(a[k], w[k], acc);
   acc += bias[(size_t)e * N + n];
   out[(size_t)row * N + n] = (EPI == 0) ? gelu_tanh_f(acc) : acc;
 }

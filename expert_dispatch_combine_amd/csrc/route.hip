@@ -639,8 +639,20 @@ __global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict
   const int t = (int)(i / E), e = (int)(i % E);
   const float* a = x + (size_t)t * h;
   const float* b = wg + (size_t)e * h;
+  // sequential fp32 FMAs over h; the loads of 8 terms go out before their FMAs
   float acc = 0.f;
-  for (int j = 0; j < h; ++j) acc = fmaf(a[j], b[j], acc);
+  int j = 0;
+  for (; j + 8 <= h; j += 8) {
+    float av[8], bv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      av[u] = a[j + u];
+      bv[u] = b[j + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = fmaf(av[u], bv[u], acc);
+  }
+  for (; j < h; ++j) acc = fmaf(a[j], b[j], acc);
   logits[i] = acc;
 }
 
