@@ -45,7 +45,10 @@
 // per-expert tile counts from `offsets`, maps its id to a logical tile with an
 // XCD-aware permutation (consecutive logical tiles run on the same XCD and
 // share its L2) and exits if it has none.  Logical tiles are ordered by
-// expert, then groups of 8 weight tiles, then row tiles fastest.
+// expert, then groups of 8 weight tiles, then row tiles fastest.  Where the
+// capacity fits one row tile of the streaming shape, every expert has one row
+// tile whatever the routing, so the map needs no `offsets` and the weight
+// prefetch starts before the expert's row range is read.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -189,11 +192,15 @@ struct StreamShape {
   static constexpr int LDS_BYTES = M1 > OUT_BYTES ? M1 : OUT_BYTES;
 };
 
+// one_rt != 0: the host guarantees that every expert's rows fit one row tile
+// (rows <= BM), so tile L is (expert L / (N/BN), weight tile L % (N/BN)) with
+// no look at `offsets`: the weight prefetch is issued before the expert's row
+// range arrives, and a workgroup of an empty expert leaves after reading it.
 template <int MT, int WN, int WK, int EPI, bool PK, int OCC>
 __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, void* __restrict__ out,
-    const int32_t* __restrict__ offsets, int E, int N, int Kd) {
+    const int32_t* __restrict__ offsets, int E, int N, int Kd, int one_rt) {
   using S = StreamShape<MT, WN, WK, OCC>;
   static_assert(S::PD % S::AD == 0 && S::PD % 2 == 0, "ring sizes");
   // the epilogue stages all BM output rows at once when they fit in 48 KB
@@ -205,8 +212,20 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
   uint16_t* act = (uint16_t*)lds;  // [2][BM rows][8 quads], swizzled
 
   const int tid = threadIdx.x;
-  if (!find_tile<S::BM, S::BN>(offsets, E, N, &tinfo, tid)) return;
-  const int e = tinfo.e, row0 = tinfo.row0, row_end = tinfo.row_end, n0 = tinfo.n0;
+  int e, row0 = 0, row_end = 0, n0;
+  if (one_rt) {
+    const int ntn = N / S::BN;
+    const int total = E * ntn;
+    const int per_xcd = (total + NXCD - 1) / NXCD;
+    const int bid = blockIdx.x;
+    const int L = bid < per_xcd * NXCD ? (bid % NXCD) * per_xcd + bid / NXCD : total;
+    if (L >= total) return;
+    e = L / ntn;
+    n0 = (L - e * ntn) * S::BN;
+  } else {
+    if (!find_tile<S::BM, S::BN>(offsets, E, N, &tinfo, tid)) return;
+    e = tinfo.e, row0 = tinfo.row0, row_end = tinfo.row_end, n0 = tinfo.n0;
+  }
   const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, kw = wave / WN;
   const int li = lane & 31, lg = lane >> 5;
@@ -222,6 +241,18 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
          (kw * S::KSTEPS * 64 + lane) * 8;
   else
     wp = W + ((size_t)e * N + n0 + wn * 32 + li) * Kd + kw * S::KW + lg * (S::KW / 2);
+  u32x4 wr[S::PD][S::KSTEPS];
+#pragma unroll
+  for (int p = 0; p < S::PD - 1; ++p)
+    if (p < nchunks)
+#pragma unroll
+      for (int q = 0; q < S::KSTEPS; ++q) wr[p][q] = *(const u32x4*)(wp + p * CSTR + q * QSTR);
+  if (one_rt) {
+    row0 = offsets[e];
+    row_end = offsets[e + 1];
+    if (row_end <= row0) return;  // empty expert (uniform)
+  }
+
   // ---- activations: this thread stages MT quads per chunk (row c/8, quad c%8)
   const uint16_t* ap[MT];
   int alds[MT];
@@ -250,13 +281,6 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
   for (int tm = 0; tm < MT; ++tm)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[tm][r] = 0.f;
-
-  u32x4 wr[S::PD][S::KSTEPS];
-#pragma unroll
-  for (int p = 0; p < S::PD - 1; ++p)
-    if (p < nchunks)
-#pragma unroll
-      for (int q = 0; q < S::KSTEPS; ++q) wr[p][q] = *(const u32x4*)(wp + p * CSTR + q * QSTR);
 
   // activations: chunk 0 straight into LDS stage 0, chunks 1 .. AD-1 into
   // register slots; chunk c+AD is always in flight while chunk c is computed
@@ -827,38 +851,43 @@ int64_t grid_for(int64_t r_max, int BM, int E, int N, int BN) {
 template <int MT, int WN, int WK, int EPI, bool PK, int OCC>
 hipError_t launch_stream(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
                          const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
-                         hipStream_t s) {
-  const int64_t grid = grid_for(r_max, 32 * MT, E, N, 32 * WN);
+                         int64_t rows_max, hipStream_t s) {
+  // every expert's rows in one row tile: static tile map (see the kernel)
+  const int one_rt = rows_max <= 32 * MT ? 1 : 0;
+  const int64_t grid = one_rt ? ((int64_t)E * (N / (32 * WN)) + NXCD - 1) / NXCD * NXCD
+                              : grid_for(r_max, 32 * MT, E, N, 32 * WN);
   hipLaunchKernelGGL((stream_gemm_kernel<MT, WN, WK, EPI, PK, OCC>), dim3((unsigned)grid),
-                     dim3(256), 0, s, A, W, bias, out, offsets, E, N, Kd);
+                     dim3(256), 0, s, A, W, bias, out, offsets, E, N, Kd, one_rt);
   return hipGetLastError();
 }
 
 template <int MT, int WN, int WK, int EPI, bool PK>
 hipError_t launch_stream_occ(bool occ1, const uint16_t* A, const uint16_t* W, const float* bias,
                              void* out, const int32_t* offsets, int E, int N, int Kd,
-                             int64_t r_max, hipStream_t s) {
+                             int64_t r_max, int64_t rows_max, hipStream_t s) {
   // built only for the tall tiles, where one workgroup per CU is the common case
   if constexpr (MT >= 4 && WN == 2)
     if (occ1)
-      return launch_stream<MT, WN, WK, EPI, PK, 1>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
-  return launch_stream<MT, WN, WK, EPI, PK, 2>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+      return launch_stream<MT, WN, WK, EPI, PK, 1>(A, W, bias, out, offsets, E, N, Kd, r_max,
+                                                   rows_max, s);
+  return launch_stream<MT, WN, WK, EPI, PK, 2>(A, W, bias, out, offsets, E, N, Kd, r_max,
+                                               rows_max, s);
 }
 
 template <int MT, int EPI, bool PK>
 hipError_t launch_stream_mt(int wn, bool occ1, const uint16_t* A, const uint16_t* W,
                             const float* bias, void* out, const int32_t* offsets, int E, int N,
-                            int Kd, int64_t r_max, hipStream_t s) {
+                            int Kd, int64_t r_max, int64_t rows_max, hipStream_t s) {
   if (wn == 4)
     return launch_stream_occ<MT, 4, 1, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                s);
+                                                rows_max, s);
   // the 4-way k split keeps MT <= 3 (its reduction and ring outgrow the registers)
   if (wn == 2 || MT >= 4)
     return launch_stream_occ<MT, 2, 2, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                s);
+                                                rows_max, s);
   if constexpr (MT < 4)
     return launch_stream_occ<MT, 1, 4, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                s);
+                                                rows_max, s);
   return hipErrorInvalidValue;
 }
 
@@ -917,7 +946,8 @@ hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* b
   const bool occ1 = mtiles * (N / (32 * wn)) <= 256;
   switch (mt) {
 #define MOE_MT_CASE(M_)                                                                    \
-    return launch_stream_mt<M_, EPI, PK>(wn, occ1, A, W, bias, out, offsets, E, N, Kd, r_max, s)
+    return launch_stream_mt<M_, EPI, PK>(wn, occ1, A, W, bias, out, offsets, E, N, Kd, r_max, \
+                                         rows_max, s)
     case 1: MOE_MT_CASE(1);
     case 2: MOE_MT_CASE(2);
     case 3: MOE_MT_CASE(3);

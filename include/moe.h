@@ -208,7 +208,9 @@ int moe_dispatch(const moe_cfg* cfg, const void* x, const int32_t* topk_idx,
  *   x_disp [R_max, h] dtype;  w1 [E, F, h] dtype;  b1 [E, F] fp32
  *   w2 [E, h, F] dtype;  b2 [E, h] fp32;  h_buf [R_max, F] dtype (scratch,
  *   holds H afterwards);  y [R_max, h] fp32.  Rows >= R are not written.
- * `capacity` bounds R_max (the same value given to moe_dispatch). */
+ * `capacity` bounds R_max and every expert's segment, offset[e+1] -
+ * offset[e] <= capacity (the same value given to moe_dispatch, whose
+ * offsets satisfy it). */
 int moe_expert_ffn(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
                    const int32_t* expert_offsets, const void* w1, const float* b1,
                    const void* w2, const float* b2, void* h_buf, float* y,
