@@ -851,9 +851,9 @@ int64_t grid_for(int64_t r_max, int BM, int E, int N, int BN) {
 template <int MT, int WN, int WK, int EPI, bool PK, int OCC>
 hipError_t launch_stream(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
                          const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
-                         int64_t rows_max, hipStream_t s) {
-  // every expert's rows in one row tile: static tile map (see the kernel)
-  const int one_rt = rows_max <= 32 * MT ? 1 : 0;
+                         bool static_map, hipStream_t s) {
+  // static_map: every expert's rows fit one row tile (see the kernel)
+  const int one_rt = static_map ? 1 : 0;
   const int64_t grid = one_rt ? ((int64_t)E * (N / (32 * WN)) + NXCD - 1) / NXCD * NXCD
                               : grid_for(r_max, 32 * MT, E, N, 32 * WN);
   hipLaunchKernelGGL((stream_gemm_kernel<MT, WN, WK, EPI, PK, OCC>), dim3((unsigned)grid),
@@ -864,30 +864,30 @@ hipError_t launch_stream(const uint16_t* A, const uint16_t* W, const float* bias
 template <int MT, int WN, int WK, int EPI, bool PK>
 hipError_t launch_stream_occ(bool occ1, const uint16_t* A, const uint16_t* W, const float* bias,
                              void* out, const int32_t* offsets, int E, int N, int Kd,
-                             int64_t r_max, int64_t rows_max, hipStream_t s) {
+                             int64_t r_max, bool static_map, hipStream_t s) {
   // built only for the tall tiles, where one workgroup per CU is the common case
   if constexpr (MT >= 4 && WN == 2)
     if (occ1)
       return launch_stream<MT, WN, WK, EPI, PK, 1>(A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                   rows_max, s);
+                                                   static_map, s);
   return launch_stream<MT, WN, WK, EPI, PK, 2>(A, W, bias, out, offsets, E, N, Kd, r_max,
-                                               rows_max, s);
+                                               static_map, s);
 }
 
 template <int MT, int EPI, bool PK>
 hipError_t launch_stream_mt(int wn, bool occ1, const uint16_t* A, const uint16_t* W,
                             const float* bias, void* out, const int32_t* offsets, int E, int N,
-                            int Kd, int64_t r_max, int64_t rows_max, hipStream_t s) {
+                            int Kd, int64_t r_max, bool static_map, hipStream_t s) {
   if (wn == 4)
     return launch_stream_occ<MT, 4, 1, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                rows_max, s);
+                                                static_map, s);
   // the 4-way k split keeps MT <= 3 (its reduction and ring outgrow the registers)
   if (wn == 2 || MT >= 4)
     return launch_stream_occ<MT, 2, 2, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                rows_max, s);
+                                                static_map, s);
   if constexpr (MT < 4)
     return launch_stream_occ<MT, 1, 4, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                rows_max, s);
+                                                static_map, s);
   return hipErrorInvalidValue;
 }
 
@@ -937,6 +937,10 @@ hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* b
   int mt = (int)((rows_max + 31) / 32);
   if (mt > 5) mt = 4;
   if (mt < 1) mt = 1;
+  // Static tile map when every expert fits one row tile and a typical
+  // expert fills at least half of it: with many empty experts their
+  // workgroups would prefetch weights for nothing.
+  const bool one_rt = rows_max <= 32 * mt && 2 * rows_typ >= 32 * mt;
   const int64_t bm = 32 * mt;
   const int64_t mtiles = (r_max + bm - 1) / bm > E ? (r_max + bm - 1) / bm : E;
   int wn = 1;
@@ -947,7 +951,7 @@ hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* b
   switch (mt) {
 #define MOE_MT_CASE(M_)                                                                    \
     return launch_stream_mt<M_, EPI, PK>(wn, occ1, A, W, bias, out, offsets, E, N, Kd, r_max, \
-                                         rows_max, s)
+                                         one_rt, s)
     case 1: MOE_MT_CASE(1);
     case 2: MOE_MT_CASE(2);
     case 3: MOE_MT_CASE(3);
