@@ -5,12 +5,14 @@ combine, plus the ledger) on one MI355X, through the C ABI of libmoe.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--mode graph]
 
 A step is one pass of the whole path over one batch of tokens: moe_route,
-moe_dispatch, moe_expert_ffn, moe_combine and the ledger (moe_ledger_launch:
-its kernels plus the copy of its counters to a page-locked host stage), all
-on one stream (--ledger-stream side moves the ledger to a second stream that
-starts after the dispatch and joins before the step ends); the host decodes
-each step's ledger (moe_ledger_finalize) while the next step runs.  Inputs
-are resident in HBM.
+moe_dispatch, moe_expert_ffn, then the combine and the ledger (its counting
+kernels, whose counters land in a page-locked host stage) in one
+moe_combine_ledger call, all on one stream.  --ledger-stream main issues
+moe_combine and moe_ledger_launch as two calls instead; side moves the
+ledger to a second stream that starts after the dispatch and joins before
+the step ends.  The host decodes every step's ledger (moe_ledger_finalize,
+into buffers allocated once) a few steps behind the device, while later
+steps run.  Inputs are resident in HBM.
 So that the 256 MB last-level cache cannot serve the weights, successive steps
 rotate over several copies of x and of all weights (>= 1 GiB in total).
 
@@ -55,9 +57,10 @@ def parse():
                         "as a server does at load time) or row-major")
     p.add_argument("--rotate-bytes", type=float, default=float(1 << 30),
                    help="total bytes of rotated input copies (defeats the 256 MB cache)")
-    p.add_argument("--ledger-stream", choices=["side", "main"], default="main",
-                   help="run the ledger's kernels on a side stream beside the FFN, or after "
-                        "the combine on the main stream")
+    p.add_argument("--ledger-stream", choices=["fused", "main", "side"], default="fused",
+                   help="fused: combine and ledger in one moe_combine_ledger call; main: "
+                        "moe_combine then moe_ledger_launch; side: the ledger on a second "
+                        "stream beside the FFN")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-next-rows", action="store_true",
                    help="skip the timings of the entry points beyond the layer step (bias "
@@ -250,7 +253,8 @@ def main():
     side_s = torch.cuda.Stream() if args.ledger_stream == "side" else None
     ledger_ws = torch.empty_like(bufs.ws)
     plans = [LayerPlan(bufs, *st, inp.src_rank, inp.owner_rank, wl.n_ep, 0.01, main=main_s,
-                       side=side_s, ledger_ws=ledger_ws, packed=packed) for st in sets]
+                       side=side_s, ledger_ws=ledger_ws, packed=packed,
+                       fused_tail=args.ledger_stream == "fused") for st in sets]
     torch.cuda.synchronize()
     done = [torch.cuda.Event() for _ in range(n_rot)]
 
@@ -275,8 +279,15 @@ def main():
                 graphs[i % n_rot].replay()
         torch.cuda.synchronize()
 
+    # The host decodes step i-lag's ledger (C moe_ledger_finalize into the
+    # plan's buffers) after issuing step i, so up to `lag` later steps stay
+    # queued on the device while it does.  A plan's stage is rewritten only
+    # when the plan is launched again, n_rot steps later, so lag < n_rot (with
+    # a single rotation set each step is decoded before the next is issued).
+    lag = min(4, n_rot - 1)
+
     def run_steps(K, events=None):
-        last = None
+        pending = []
         with torch.cuda.stream(main_s):
             for i in range(K):
                 j = i % n_rot
@@ -285,11 +296,15 @@ def main():
                 else:
                     plans[j].launch(events[i] if events else None)
                 done[j].record(main_s)
-                if last is not None:           # decode the previous step's ledger
-                    done[last].synchronize()
-                    plans[last].ledger()
-                last = j
-        return last
+                pending.append(j)
+                if len(pending) > lag:
+                    old = pending.pop(0)
+                    done[old].synchronize()
+                    plans[old].decode()
+            for old in pending:
+                done[old].synchronize()
+                plans[old].decode()
+        return j
 
     K = args.steps
     torch.cuda.synchronize()
@@ -360,7 +375,8 @@ def main():
         "accepted_routes_per_s": R * K / elapsed,
         "eager_tokens_per_s": wl.T * K / elapsed_eager,
         "per_call_ms": {"route": t_route, "dispatch": t_disp, "expert_ffn": t_ffn,
-                        "combine": t_comb},
+                        ("combine_ledger" if args.ledger_stream == "fused" else "combine"):
+                        t_comb},
         "roofline": roof,
         "ledger": {k: led[k] for k in ("accepted_routes", "overflow", "balance_ratio",
                                         "local_hit_ratio", "l_aux")},

@@ -25,6 +25,7 @@ EXPORTED_SYMBOLS = (
     "moe_ledger_stage_bytes", "moe_ledger_launch", "moe_ledger_finalize",
     "moe_expert_ffn_packed", "moe_pack_expert_weights", "moe_bias_update",
     "moe_fp8_scale", "moe_dispatch_fp8", "moe_fp8_dequantize", "moe_recommend_plan",
+    "moe_combine_ledger",
 )
 
 
@@ -109,6 +110,9 @@ def load_library():
     lib.moe_ledger_launch.restype = ctypes.c_int
     lib.moe_ledger_launch.argtypes = [cfgp, P, P, P, P, P, ctypes.c_int32, P, ctypes.c_size_t,
                                       P, ctypes.c_size_t, P]
+    lib.moe_combine_ledger.restype = ctypes.c_int
+    lib.moe_combine_ledger.argtypes = [cfgp, P, P, P, P, P, P, P, ctypes.c_int32, P,
+                                       ctypes.c_size_t, P, ctypes.c_size_t, P]
     lib.moe_ledger_finalize.restype = ctypes.c_int
     lib.moe_ledger_finalize.argtypes = [cfgp, _I64, ctypes.c_int32, _F64, P,
                                         ctypes.POINTER(MoeLedger), P, P, P, P]
@@ -372,6 +376,25 @@ def moe_ledger_launch(cfg: MoeCfg, topk_idx, topk_gate, route_row, src_rank, own
                                _ptr(owner_rank, "i32", cfg, "owner_rank"), int(n_ep), hp, hb,
                                wsp, wsb, _stream(stream))
     _check("moe_ledger_launch", st)
+
+
+def moe_combine_ledger(cfg: MoeCfg, y, route_row, topk_gate, out, topk_idx, src_rank,
+                       owner_rank, n_ep: int, host_stage: torch.Tensor, ws=None,
+                       stream=None) -> None:
+    """moe_combine and moe_ledger_launch in one call (one launch up to 4096
+    routes); `host_stage` as for moe_ledger_launch."""
+    lib = load_library()
+    wsp, wsb = _ws(ws)
+    hp, hb = _host_ptr(host_stage, "host_stage")
+    st = lib.moe_combine_ledger(ctypes.byref(cfg), _ptr(y, "f32", cfg, "y"),
+                                _ptr(route_row, "i32", cfg, "route_row"),
+                                _ptr(topk_gate, "f32", cfg, "topk_gate"),
+                                _ptr(out, "f32", cfg, "out"),
+                                _ptr(topk_idx, "i32", cfg, "topk_idx"),
+                                _ptr(src_rank, "i32", cfg, "src_rank"),
+                                _ptr(owner_rank, "i32", cfg, "owner_rank"), int(n_ep), hp, hb,
+                                wsp, wsb, _stream(stream))
+    _check("moe_combine_ledger", st)
 
 
 def moe_ledger_finalize(cfg: MoeCfg, capacity: int, n_ep: int, alpha: float,

@@ -311,6 +311,35 @@ int moe_ledger_launch(const moe_cfg* cfg, const int32_t* topk_idx, const float* 
   return MOE_OK;
 }
 
+int moe_combine_ledger(const moe_cfg* cfg, const float* y, const int32_t* route_row,
+                       const float* topk_gate, float* out, const int32_t* topk_idx,
+                       const int32_t* src_rank, const int32_t* owner_rank, int32_t n_ep,
+                       void* host_stage, size_t stage_bytes, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int st = ledger_args(cfg, topk_idx, topk_gate, route_row, src_rank, owner_rank, n_ep, ws,
+                       ws_bytes);
+  if (st != MOE_OK) return st;
+  if (cfg->T > 0 && !out) return MOE_ERR_INVALID_ARG;
+  if (!host_stage) return MOE_ERR_INVALID_ARG;
+  if (stage_bytes < ledger_final_bytes(cfg->E, n_ep)) return MOE_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  void* mapped = nullptr;  // as in moe_ledger_launch
+  if (hipHostGetDevicePointer(&mapped, host_stage, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    mapped = nullptr;
+  }
+  void* fin = nullptr;
+  size_t fin_bytes = 0;
+  // y may be NULL only when nothing was accepted; the kernels never read it then
+  st = hip_status(launch_combine_ledger(y, route_row, topk_gate, out, topk_idx, src_rank,
+                                        owner_rank, cfg->T, cfg->K, cfg->h, cfg->E, n_ep, ws,
+                                        mapped, &fin, &fin_bytes, s));
+  if (st != MOE_OK || mapped) return st;
+  if (hipMemcpyAsync(host_stage, fin, fin_bytes, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 int moe_ledger_finalize(const moe_cfg* cfg, int64_t capacity, int32_t n_ep, double alpha,
                         const void* host_stage, moe_ledger_t* out, int64_t* loads, double* f,
                         double* P, int64_t* pair_routes) {

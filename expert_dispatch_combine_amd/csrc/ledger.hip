@@ -18,10 +18,11 @@
 // Device part: one workgroup per 512 routes builds LDS histograms and a
 // second kernel adds the per-block partials (one wave per output value).  Up
 // to kSmallLedgerRoutes routes one workgroup takes them all and writes the
-// final area itself.  The final area may be page-locked host memory (its
-// device address), which spares a copy.  The host finishes the few scalar
-// formulas in float64.
-#include "moe_internal.hpp"
+// final area itself; that workgroup can also run as block 0 of the combine's
+// launch (combine_ledger_kernel), beside the combine's own workgroups.  The
+// final area may be page-locked host memory (its device address), which
+// spares a copy.  The host finishes the few scalar formulas in float64.
+#include "combine_block.hpp"
 
 namespace moe {
 
@@ -78,23 +79,27 @@ __device__ __forceinline__ unsigned long long gate_fixed(float g) {
   return __double2ull_rn((double)g * 4294967296.0);
 }
 
-// RPB routes per workgroup.  FINAL (a one-workgroup launch): write the final
-// area `fin` directly instead of the per-block partials.
+// LDS of one ledger workgroup, carved from a byte array (8-byte sums first).
+constexpr int kLedgerLdsBytes = kMaxExperts * (8 + 4 + 4) + kMaxRanks * kMaxRanks * 4 + LC_N * 4;
+
+// Workgroup b of the ledger: RPB routes from b * RPB.  FINAL (one workgroup
+// takes every route): write the final area `fin` directly instead of the
+// per-block partials.  `lds`: kLedgerLdsBytes, 8-byte aligned.
 template <int RPB, bool FINAL>
-__global__ __launch_bounds__(256) void ledger_partial_kernel(
-    const int32_t* __restrict__ idx, const float* __restrict__ gate,
+__device__ __forceinline__ void ledger_block(
+    int b, const int32_t* __restrict__ idx, const float* __restrict__ gate,
     const int32_t* __restrict__ route_row, const int32_t* __restrict__ src,
     const int32_t* __restrict__ owner, int64_t A, int K, int E, int n_ep,
     int32_t* __restrict__ blk_load, uint64_t* __restrict__ blk_P,
-    int64_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_pair, char* __restrict__ fin) {
+    int64_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_pair, char* __restrict__ fin,
+    char* lds) {
   constexpr int PER_THREAD = RPB / 256;
-  __shared__ int s_load[kMaxExperts];
-  __shared__ unsigned long long s_P[kMaxExperts];
-  __shared__ int s_owner[kMaxExperts];
-  __shared__ int s_pair[kMaxRanks * kMaxRanks];
-  __shared__ int s_cnt[LC_N];
+  unsigned long long* s_P = (unsigned long long*)lds;
+  int* s_load = (int*)(lds + kMaxExperts * 8);
+  int* s_owner = s_load + kMaxExperts;
+  int* s_pair = s_owner + kMaxExperts;
+  int* s_cnt = s_pair + kMaxRanks * kMaxRanks;
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
   const int np = n_ep * n_ep;
   for (int e = tid; e < E; e += 256) {
     s_load[e] = 0;
@@ -188,6 +193,39 @@ __global__ __launch_bounds__(256) void ledger_partial_kernel(
   if (tid < LC_N) blk_cnt[(size_t)b * LC_N + tid] = s_cnt[tid];
 }
 
+template <int RPB, bool FINAL>
+__global__ __launch_bounds__(256) void ledger_partial_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ gate,
+    const int32_t* __restrict__ route_row, const int32_t* __restrict__ src,
+    const int32_t* __restrict__ owner, int64_t A, int K, int E, int n_ep,
+    int32_t* __restrict__ blk_load, uint64_t* __restrict__ blk_P,
+    int64_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_pair, char* __restrict__ fin) {
+  __shared__ __attribute__((aligned(16))) char lds[kLedgerLdsBytes];
+  ledger_block<RPB, FINAL>(blockIdx.x, idx, gate, route_row, src, owner, A, K, E, n_ep,
+                           blk_load, blk_P, blk_cnt, blk_pair, fin, lds);
+}
+
+// The combine and the one-workgroup ledger in one launch: block 0 (dispatched
+// first, and the longest) is the ledger, blocks 1.. the combine's workgroups.
+// The two read the same routes and write disjoint outputs.
+template <bool VEC, int U>
+__global__ __launch_bounds__(256) void combine_ledger_kernel(
+    const float* __restrict__ y, const int32_t* __restrict__ route_row,
+    const float* __restrict__ gate, float* __restrict__ out, int T, int K, int h, int TB,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ src,
+    const int32_t* __restrict__ owner, int E, int n_ep, char* __restrict__ fin) {
+  constexpr int LDS = kLedgerLdsBytes > kCombineLdsBytes ? kLedgerLdsBytes : kCombineLdsBytes;
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  if (blockIdx.x == 0) {
+    ledger_block<kSmallLedgerRoutes, true>(0, idx, gate, route_row, src, owner, (int64_t)T * K,
+                                           K, E, n_ep, nullptr, nullptr, nullptr, nullptr, fin,
+                                           lds);
+    return;
+  }
+  combine_tokens<VEC, U>(blockIdx.x - 1, y, route_row, gate, out, T, K, h, TB, (int*)lds,
+                         (float*)(lds + kMaxTB * kMaxTopK * 4));
+}
+
 // final[q] = sum over blocks of the per-block partial q; one wave per q, its
 // lanes take blocks lane, lane + 64, ... (integers: any order is exact)
 __global__ __launch_bounds__(256) void ledger_reduce_kernel(
@@ -254,6 +292,31 @@ hipError_t launch_ledger(const int32_t* idx, const float* gate, const int32_t* r
   const int items = 2 * E + LC_N + n_ep * n_ep;
   hipLaunchKernelGGL(ledger_reduce_kernel, dim3((items + 3) / 4), dim3(256), 0, s, nb, E, n_ep,
                      w.blk_load, w.blk_P, w.blk_cnt, w.blk_pair, fin);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_ledger(const float* y, const int32_t* route_row, const float* gate,
+                                 float* out, const int32_t* idx, const int32_t* src,
+                                 const int32_t* owner, int T, int K, int h, int E, int n_ep,
+                                 void* ws, void* fin_dst, void** final_area_out,
+                                 size_t* final_bytes, hipStream_t s) {
+  const int64_t A = (int64_t)T * K;
+  if (A == 0 || h == 0 || A > kSmallLedgerRoutes) {  // two launches
+    hipError_t err = launch_combine(y, route_row, gate, out, T, K, h, s);
+    if (err != hipSuccess) return err;
+    return launch_ledger(idx, gate, route_row, src, owner, T, K, E, n_ep, ws, fin_dst,
+                         final_area_out, final_bytes, s);
+  }
+  LedgerWs w = carve(ws, A, E, n_ep);
+  char* fin = fin_dst ? (char*)fin_dst : w.fin;
+  *final_area_out = fin;
+  *final_bytes = w.fin_bytes;
+  const CombineShape c = combine_shape(T, h);
+  with_combine_variant(c, [&](auto vec, auto u) {
+    hipLaunchKernelGGL((combine_ledger_kernel<decltype(vec)::value, decltype(u)::value>),
+                       dim3(c.grid + 1), dim3(256), 0, s, y, route_row, gate, out, T, K, h,
+                       c.TB, idx, src, owner, E, n_ep, fin);
+  });
   return hipGetLastError();
 }
 

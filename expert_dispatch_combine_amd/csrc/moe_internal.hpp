@@ -214,5 +214,13 @@ hipError_t launch_ledger(const int32_t* idx, const float* gate, const int32_t* r
                          const int32_t* src, const int32_t* owner, int T, int K, int E,
                          int n_ep, void* ws, void* fin_dst, void** final_area,
                          size_t* final_bytes, hipStream_t s);
+// The combine and the ledger of the same routes: one launch up to
+// kSmallLedgerRoutes routes (the ledger's one workgroup beside the combine's),
+// else launch_combine then launch_ledger.  Same results as those two.
+hipError_t launch_combine_ledger(const float* y, const int32_t* route_row, const float* gate,
+                                 float* out, const int32_t* idx, const int32_t* src,
+                                 const int32_t* owner, int T, int K, int h, int E, int n_ep,
+                                 void* ws, void* fin_dst, void** final_area,
+                                 size_t* final_bytes, hipStream_t s);
 
 }  // namespace moe

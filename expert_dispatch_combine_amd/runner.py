@@ -13,7 +13,8 @@ import ctypes
 
 import torch
 
-from ._binding import (MOE_BF16, MoeCfg, MoeError, _ptr, _ws, load_library, moe_capacity,
+from ._binding import (_F64, _I64, MOE_BF16, MoeCfg, MoeError, MoeLedger, _ptr, _ws,
+                       load_library, moe_capacity,
                        moe_combine, moe_dispatch, moe_expert_ffn, moe_expert_ffn_packed,
                        moe_ledger, moe_ledger_finalize, moe_ledger_stage_bytes, moe_max_rows,
                        moe_pack_expert_weights, moe_route, moe_workspace_bytes)
@@ -99,7 +100,8 @@ class LayerPlan:
     device half with the copy of its counters to a page-locked host stage --
     marshalled once.  `launch()` enqueues it with bare C calls; the ledger
     runs on `side` (after the dispatch, beside the FFN) when given, joined back
-    into `main` before launch() returns.  After the work has completed,
+    into `main` before launch() returns; with fused_tail it runs with the
+    combine in one moe_combine_ledger call.  After the work has completed,
     `ledger()` decodes the stage on the host.
 
     The plan does not own the tensors: they must outlive it and keep their
@@ -109,12 +111,17 @@ class LayerPlan:
 
     def __init__(self, b: LayerBuffers, x, w_gate, logit_bias, w1, b1, w2, b2, src_rank,
                  owner_rank, n_ep: int, alpha: float = 0.01, main=None, side=None,
-                 ledger_ws=None, packed: bool = False, logits_in: bool = False):
+                 ledger_ws=None, packed: bool = False, logits_in: bool = False,
+                 fused_tail: bool = False):
         lib = load_library()
         cfg = b.cfg
         self.b, self.cfg, self.n_ep, self.alpha = b, cfg, int(n_ep), float(alpha)
         self.main = main if main is not None else torch.cuda.current_stream()
         self.side = side
+        if fused_tail and side is not None:
+            raise ValueError("fused_tail runs the ledger with the combine on `main`: no side "
+                             "stream")
+        self.fused_tail = bool(fused_tail)
         self.stage = torch.empty((moe_ledger_stage_bytes(cfg, n_ep),), dtype=torch.uint8,
                                  pin_memory=True)
         self.ledger_ws = ledger_ws if ledger_ws is not None else (
@@ -154,6 +161,18 @@ class LayerPlan:
             p(b.route_row, "i32", "route_row"), p(src_rank, "i32", "src_rank"),
             p(owner_rank, "i32", "owner_rank"), self.n_ep,
             ctypes.c_void_p(self.stage.data_ptr()), self.stage.numel(), lwsp, lwsb, ls))
+        self.combine_ledger = (lib.moe_combine_ledger, (
+            c, p(b.y, "f32", "y"), p(b.route_row, "i32", "route_row"),
+            p(b.topk_gate, "f32", "topk_gate"), p(b.out, "f32", "out"),
+            p(b.topk_idx, "i32", "topk_idx"), p(src_rank, "i32", "src_rank"),
+            p(owner_rank, "i32", "owner_rank"), self.n_ep,
+            ctypes.c_void_p(self.stage.data_ptr()), self.stage.numel(), lwsp, lwsb, ms))
+        # moe_ledger_finalize into buffers allocated once (decode() per step)
+        E, ne = int(cfg.E), self.n_ep
+        self._fin = (MoeLedger(), (_I64 * E)(), (_F64 * E)(), (_F64 * E)(), (_I64 * (ne * ne))())
+        self.finalize = (lib.moe_ledger_finalize, (
+            c, int(b.capacity), ne, self.alpha, ctypes.c_void_p(self.stage.data_ptr()),
+            ctypes.byref(self._fin[0]), *self._fin[1:]))
         self.ev_dispatched = torch.cuda.Event()
         self.ev_ledger = torch.cuda.Event()
 
@@ -183,6 +202,11 @@ class LayerPlan:
         self._call("moe_expert_ffn", self.ffn)
         if events:
             events[3].record(m)
+        if self.fused_tail:  # combine and ledger in one call (one launch when small)
+            self._call("moe_combine_ledger", self.combine_ledger)
+            if events:
+                events[4].record(m)
+            return
         self._call("moe_combine", self.combine)
         if events:
             events[4].record(m)
@@ -190,6 +214,16 @@ class LayerPlan:
             self._call("moe_ledger_launch", self.ledger_launch)
         else:
             m.wait_event(self.ev_ledger)
+
+    def decode(self) -> int:
+        """moe_ledger_finalize of the completed stage into the plan's own host
+        buffers (no Python objects built); returns its status (0, or 1/2
+        when the batch held invalid ranks / expert ids)."""
+        fn, args = self.finalize
+        st = fn(*args)
+        if st not in (0, 1, 2):
+            raise MoeError("moe_ledger_finalize", st)
+        return st
 
     def ledger(self, **kw) -> dict:
         """Decode the host stage (the step's work must have completed)."""

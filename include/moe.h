@@ -284,6 +284,21 @@ int moe_ledger_finalize(const moe_cfg* cfg, int64_t capacity, int32_t n_ep, doub
                         const void* host_stage, moe_ledger_t* out, int64_t* loads,
                         double* f, double* P, int64_t* pair_routes);
 
+/* moe_combine and moe_ledger_launch of the same routes in one call ([EP46]
+ * combine_expert_outputs and summarize; [EPC] Combine; [EP47] summarize):
+ * the arguments of both, the same `out` and the same `host_stage` contents
+ * (decode them with moe_ledger_finalize once the stream has passed the
+ * call).  Up to 4096 routes (T*K) both run in ONE launch, the ledger's
+ * single workgroup beside the combine's, which spares the second launch's
+ * fixed cost; above that it enqueues the two calls' kernels in turn.  The
+ * workspace is the ledger's (moe_workspace_bytes) and must not be reused
+ * before the stage copy is done, as for moe_ledger_launch. */
+int moe_combine_ledger(const moe_cfg* cfg, const float* y, const int32_t* route_row,
+                       const float* topk_gate, float* out, const int32_t* topk_idx,
+                       const int32_t* src_rank, const int32_t* owner_rank, int32_t n_ep,
+                       void* host_stage, size_t stage_bytes, void* ws, size_t ws_bytes,
+                       void* stream);
+
 /* Joint parallel-plan decision over one ledger ([EP46] TODO 3, joint
  * decision; thresholds default to that page's):
  *   MOE_PLAN_ACCEPT  no overflow, balance_ratio <= 1.2 and cross-rank share

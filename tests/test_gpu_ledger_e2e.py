@@ -135,6 +135,64 @@ def test_ledger_empty_and_errors():
     assert g["return_status"] == 1
 
 
+@pytest.mark.parametrize("T,h,E,K,n_ep,cf,dtype,pinned", [
+    (2048, 768, 16, 1, 8, 1.25, "bf16", True),    # one launch
+    (2048, 768, 16, 2, 8, 0.6, "bf16", True),     # 4096 routes: still one launch, drops
+    (2049, 64, 16, 2, 4, 1.0, "bf16", False),     # 4098 routes: two launches, copied stage
+    (100, 7168, 64, 2, 8, 1.0, "f32", True),      # one token per combine workgroup (U = 7)
+    (37, 30, 3, 3, 2, 0.5, "f32", False),         # scalar rows, K = E, heavy drops
+    (1, 64, 1, 1, 1, 1.0, "bf16", True)])
+def test_combine_ledger_equals_the_two_calls(T, h, E, K, n_ep, cf, dtype, pinned):
+    """moe_combine_ledger gives the same `out` (bit for bit) and the same stage
+    bytes as moe_combine followed by moe_ledger_launch, and its ledger equals
+    the oracle's."""
+    banner(f"combine+ledger T={T} h={h} E={E} K={K} pinned={pinned}")
+    rng = np.random.default_rng(T * 31 + h)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    gate = rng.random((T, K)).astype(np.float32)
+    cap = O.capacity(T * K, E, cf)
+    sl = O.slot_routes(idx, E, cap)
+    src = rng.integers(0, n_ep, T).astype(np.int32)
+    owner = (np.arange(E) % n_ep).astype(np.int32)
+    mc = M.MoeCfg.make(T, h, E, K, 64, dtype, cf)
+    R = max(int(sl["R"]), 1)
+    y = torch.randn(R, h, dtype=torch.float32, device="cuda")
+    d = dict(idx=to_dev(idx, torch.int32), gate=to_dev(gate, torch.float32),
+             row=to_dev(sl["route_row"], torch.int32), src=to_dev(src, torch.int32),
+             owner=to_dev(owner, torch.int32))
+    ws = torch.empty(M.moe_workspace_bytes(mc), dtype=torch.uint8, device="cuda")
+    nst = M.moe_ledger_stage_bytes(mc, n_ep)
+    st_two = torch.zeros((nst,), dtype=torch.uint8, pin_memory=pinned)
+    st_one = torch.full((nst,), 0xAB, dtype=torch.uint8, pin_memory=pinned)
+    out_two = torch.empty(T, h, dtype=torch.float32, device="cuda")
+    out_one = torch.full((T, h), float("nan"), dtype=torch.float32, device="cuda")
+    M.moe_combine(mc, y, d["row"], d["gate"], out_two)
+    M.moe_ledger_launch(mc, d["idx"], d["gate"], d["row"], d["src"], d["owner"], n_ep, st_two,
+                        ws)
+    torch.cuda.synchronize()
+    M.moe_combine_ledger(mc, y, d["row"], d["gate"], out_one, d["idx"], d["src"], d["owner"],
+                         n_ep, st_one, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_one, out_two)
+    assert torch.equal(st_one, st_two)
+    g = M.moe_ledger_finalize(mc, cap, n_ep, 0.01, st_one)
+    o = O.ledger(idx, gate, sl["route_row"], cap, src, owner, n_ep, h, 2 if dtype == "bf16" else 4)
+    _compare_ledger(g, o)
+
+
+def test_combine_ledger_empty_batch():
+    banner("combine+ledger empty")
+    mc = M.MoeCfg.make(0, 64, 4, 2, 64, "bf16", 1.0)
+    ws = torch.empty(M.moe_workspace_bytes(mc), dtype=torch.uint8, device="cuda")
+    owner = to_dev(np.arange(4) % 2, torch.int32)
+    stage = torch.full((M.moe_ledger_stage_bytes(mc, 2),), 0xAB, dtype=torch.uint8,
+                       pin_memory=True)
+    M.moe_combine_ledger(mc, None, None, None, None, None, None, owner, 2, stage, ws)
+    torch.cuda.synchronize()
+    g = M.moe_ledger_finalize(mc, 0, 2, 0.01, stage)
+    assert g["total_routes"] == 0 and g["loads"] == [0] * 4 and g["l_aux"] == 0.0
+
+
 # ------------------------------------------------------------------ the layer
 class _HostExperts:
     """Per-expert float64 host copies of device weights, fetched on demand."""

@@ -28,10 +28,16 @@ def _same(a, c):
     assert a["acc"] == c["acc"] and a["P"] == c["P"] and a["loads"] == c["loads"]
 
 
-@pytest.mark.parametrize("cid,packed", [(1, False), (2, False), (2, True), (3, True), (4, True),
-                                        (5, True)])
-def test_plan_and_graph_replay_match_eager(cid, packed):
-    banner(f"plan/graph config {cid} packed={packed}")
+@pytest.mark.parametrize("cid,packed,tail", [(1, False, "side"), (2, False, "side"),
+                                             (2, True, "side"), (3, True, "side"),
+                                             (4, True, "side"), (5, True, "side"),
+                                             (1, False, "fused"), (2, True, "fused"),
+                                             (5, True, "fused")])
+def test_plan_and_graph_replay_match_eager(cid, packed, tail):
+    """tail "side": the ledger on a second stream beside the FFN; "fused":
+    combine and ledger in one moe_combine_ledger call (one launch for
+    workloads 1 and 2, two for workload 5's 98304 routes)."""
+    banner(f"plan/graph config {cid} packed={packed} tail={tail}")
     inp = device_inputs(cid)
     cfg = inp.cfg
     b = buffers_for(cfg)
@@ -44,8 +50,9 @@ def test_plan_and_graph_replay_match_eager(cid, packed):
     ref = _snapshot(b, ref_led)
 
     main, side = torch.cuda.Stream(), torch.cuda.Stream()
-    plan = LayerPlan(b, *args, inp.src_rank, inp.owner_rank, cfg.n_ep, main=main, side=side,
-                     packed=packed)
+    plan = LayerPlan(b, *args, inp.src_rank, inp.owner_rank, cfg.n_ep, main=main,
+                     side=side if tail == "side" else None, packed=packed,
+                     fused_tail=tail == "fused")
     b.out.zero_()
     with torch.cuda.stream(main):
         plan.launch()
