@@ -5,9 +5,12 @@ combine, plus the ledger) on one MI355X, through the C ABI of libmoe.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--mode graph]
 
 A step is one pass of the whole path over one batch of tokens: moe_route,
-moe_dispatch, moe_expert_ffn, then the combine and the ledger (its counting
-kernels, whose counters land in a page-locked host stage) in one
-moe_combine_ledger call, all on one stream.  --ledger-stream main issues
+moe_dispatch (routing metadata), moe_expert_ffn_rows (the expert FFN, whose
+first GEMM gathers each dispatched row x[row_token[r]] in its own loads),
+then the combine and the ledger (its counting kernels, whose counters land
+in a page-locked host stage) in one moe_combine_ledger call, all on one
+stream.  --gather dispatch has moe_dispatch copy the rows into x_disp for
+moe_expert_ffn_packed instead.  --ledger-stream main issues
 moe_combine and moe_ledger_launch as two calls instead; side moves the
 ledger to a second stream that starts after the dispatch and joins before
 the step ends.  The host decodes every step's ledger (moe_ledger_finalize,
@@ -61,6 +64,9 @@ def parse():
                    help="fused: combine and ledger in one moe_combine_ledger call; main: "
                         "moe_combine then moe_ledger_launch; side: the ledger on a second "
                         "stream beside the FFN")
+    p.add_argument("--gather", choices=["ffn", "dispatch"], default="ffn",
+                   help="ffn: the first GEMM's loads gather the dispatched rows "
+                        "(moe_expert_ffn_rows); dispatch: moe_dispatch copies them into x_disp")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-next-rows", action="store_true",
                    help="skip the timings of the entry points beyond the layer step (bias "
@@ -254,7 +260,8 @@ def main():
     ledger_ws = torch.empty_like(bufs.ws)
     plans = [LayerPlan(bufs, *st, inp.src_rank, inp.owner_rank, wl.n_ep, 0.01, main=main_s,
                        side=side_s, ledger_ws=ledger_ws, packed=packed,
-                       fused_tail=args.ledger_stream == "fused") for st in sets]
+                       fused_tail=args.ledger_stream == "fused",
+                       gather_in_ffn=args.gather == "ffn") for st in sets]
     torch.cuda.synchronize()
     done = [torch.cuda.Event() for _ in range(n_rot)]
 
@@ -369,7 +376,7 @@ def main():
                                f"cf={wl.cf}", "T": wl.T, "h": wl.h, "E": wl.E, "K": wl.K,
                    "F": wl.F, "capacity_factor": wl.cf, "capacity": cap, "n_ep": wl.n_ep,
                    "mode": args.mode, "weights": "packed" if packed else "row-major",
-                   "ledger_stream": args.ledger_stream,
+                   "ledger_stream": args.ledger_stream, "gather": args.gather,
                    "rotated_copies": n_rot, "parallelism": "single GPU"},
         "routes_per_s": wl.A * K / elapsed,
         "accepted_routes_per_s": R * K / elapsed,

@@ -25,7 +25,7 @@ EXPORTED_SYMBOLS = (
     "moe_ledger_stage_bytes", "moe_ledger_launch", "moe_ledger_finalize",
     "moe_expert_ffn_packed", "moe_pack_expert_weights", "moe_bias_update",
     "moe_fp8_scale", "moe_dispatch_fp8", "moe_fp8_dequantize", "moe_recommend_plan",
-    "moe_combine_ledger",
+    "moe_combine_ledger", "moe_expert_ffn_rows",
 )
 
 
@@ -116,6 +116,8 @@ def load_library():
     lib.moe_ledger_finalize.restype = ctypes.c_int
     lib.moe_ledger_finalize.argtypes = [cfgp, _I64, ctypes.c_int32, _F64, P,
                                         ctypes.POINTER(MoeLedger), P, P, P, P]
+    lib.moe_expert_ffn_rows.restype = ctypes.c_int
+    lib.moe_expert_ffn_rows.argtypes = [cfgp, _I64, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P]
     lib.moe_expert_ffn_packed.restype = ctypes.c_int
     lib.moe_expert_ffn_packed.argtypes = [cfgp, _I64, P, P, P, P, P, P, P, P, P]
     lib.moe_pack_expert_weights.restype = ctypes.c_int
@@ -302,6 +304,20 @@ def moe_expert_ffn_packed(cfg: MoeCfg, capacity: int, x_disp, expert_offsets, w1
                                    _ptr(b2, "f32", cfg, "b2"), _ptr(h_buf, "act", cfg, "h_buf"),
                                    _ptr(y, "f32", cfg, "y"), _stream(stream))
     _check("moe_expert_ffn_packed", st)
+
+
+def moe_expert_ffn_rows(cfg: MoeCfg, capacity: int, x, row_token, expert_offsets, w1, b1, w2,
+                        b2, h_buf, y, packed: bool = False, stream=None) -> None:
+    """The expert FFN on x[row_token[r]] (the dispatch gather done by the FFN)."""
+    lib = load_library()
+    st = lib.moe_expert_ffn_rows(ctypes.byref(cfg), int(capacity), _ptr(x, "act", cfg, "x"),
+                                 _ptr(row_token, "i32", cfg, "row_token"),
+                                 _ptr(expert_offsets, "i32", cfg, "expert_offsets"),
+                                 _ptr(w1, "act", cfg, "w1"), _ptr(b1, "f32", cfg, "b1"),
+                                 _ptr(w2, "act", cfg, "w2"), _ptr(b2, "f32", cfg, "b2"),
+                                 _ptr(h_buf, "act", cfg, "h_buf"), _ptr(y, "f32", cfg, "y"),
+                                 int(bool(packed)), _stream(stream))
+    _check("moe_expert_ffn_rows", st)
 
 
 def moe_pack_expert_weights(cfg: MoeCfg, w1, w2, w1_packed, w2_packed, stream=None) -> None:

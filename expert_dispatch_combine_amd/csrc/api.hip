@@ -132,7 +132,8 @@ int moe_dispatch(const moe_cfg* cfg, const void* x, const int32_t* topk_idx, int
   const int64_t rmax = rows_max(cfg, capacity);
   if (!expert_offsets || !ws) return MOE_ERR_INVALID_ARG;
   if (A > 0 && (!topk_idx || !route_rank || !route_row)) return MOE_ERR_INVALID_ARG;
-  if (rmax > 0 && (!x || !x_disp || !row_token)) return MOE_ERR_INVALID_ARG;
+  // x_disp == NULL: routing metadata only (x is then not read)
+  if (rmax > 0 && (!row_token || (x_disp && !x))) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < moe_workspace_bytes(cfg)) return MOE_ERR_SHAPE;
   const int64_t row_bytes = (int64_t)cfg->h * elem_bytes(cfg);
   return hip_status(launch_dispatch(x, topk_idx, A, cfg->K, cfg->E, capacity, row_bytes, rmax,
@@ -189,10 +190,12 @@ int moe_fp8_dequantize(const moe_cfg* cfg, int64_t capacity, const uint8_t* x_di
                                           (uint16_t*)x_disp, (hipStream_t)stream));
 }
 
+// row_token == NULL: x_disp holds the dispatched rows; else x_disp is the
+// token matrix x [T, h] and row r reads x[row_token[r]].
 static int expert_ffn_common(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
-                             const int32_t* expert_offsets, const void* w1, const float* b1,
-                             const void* w2, const float* b2, void* h_buf, float* y,
-                             bool packed, void* stream) {
+                             const int32_t* row_token, const int32_t* expert_offsets,
+                             const void* w1, const float* b1, const void* w2, const float* b2,
+                             void* h_buf, float* y, bool packed, void* stream) {
   int st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if (capacity < 0) return MOE_ERR_INVALID_ARG;
@@ -206,29 +209,40 @@ static int expert_ffn_common(const moe_cfg* cfg, int64_t capacity, const void* x
     if (!aligned16(x_disp) || !aligned16(w1) || !aligned16(w2) || !aligned16(h_buf) ||
         !aligned16(y) || !aligned16(b1) || !aligned16(b2))
       return MOE_ERR_INVALID_ARG;
-    return hip_status(launch_ffn_bf16((const uint16_t*)x_disp, expert_offsets,
+    return hip_status(launch_ffn_bf16((const uint16_t*)x_disp, row_token, expert_offsets,
                                       (const uint16_t*)w1, b1, (const uint16_t*)w2, b2,
                                       (uint16_t*)h_buf, y, cfg->E, cfg->h, cfg->F,
                                       routes_of(cfg), capacity, rmax, packed, s));
   }
-  return hip_status(launch_ffn_f32((const float*)x_disp, expert_offsets, (const float*)w1, b1,
-                                   (const float*)w2, b2, (float*)h_buf, y, cfg->E, cfg->h,
-                                   cfg->F, rmax, s));
+  return hip_status(launch_ffn_f32((const float*)x_disp, row_token, expert_offsets,
+                                   (const float*)w1, b1, (const float*)w2, b2, (float*)h_buf, y,
+                                   cfg->E, cfg->h, cfg->F, rmax, s));
 }
 
 int moe_expert_ffn(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
                    const int32_t* expert_offsets, const void* w1, const float* b1,
                    const void* w2, const float* b2, void* h_buf, float* y, void* stream) {
-  return expert_ffn_common(cfg, capacity, x_disp, expert_offsets, w1, b1, w2, b2, h_buf, y,
-                           false, stream);
+  return expert_ffn_common(cfg, capacity, x_disp, nullptr, expert_offsets, w1, b1, w2, b2, h_buf,
+                           y, false, stream);
 }
 
 int moe_expert_ffn_packed(const moe_cfg* cfg, int64_t capacity, const void* x_disp,
                           const int32_t* expert_offsets, const void* w1_packed,
                           const float* b1, const void* w2_packed, const float* b2,
                           void* h_buf, float* y, void* stream) {
-  return expert_ffn_common(cfg, capacity, x_disp, expert_offsets, w1_packed, b1, w2_packed,
-                           b2, h_buf, y, true, stream);
+  return expert_ffn_common(cfg, capacity, x_disp, nullptr, expert_offsets, w1_packed, b1,
+                           w2_packed, b2, h_buf, y, true, stream);
+}
+
+int moe_expert_ffn_rows(const moe_cfg* cfg, int64_t capacity, const void* x,
+                        const int32_t* row_token, const int32_t* expert_offsets, const void* w1,
+                        const float* b1, const void* w2, const float* b2, void* h_buf, float* y,
+                        int32_t packed, void* stream) {
+  const int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (capacity >= 0 && rows_max(cfg, capacity) > 0 && !row_token) return MOE_ERR_INVALID_ARG;
+  return expert_ffn_common(cfg, capacity, x, row_token, expert_offsets, w1, b1, w2, b2, h_buf,
+                           y, packed != 0, stream);
 }
 
 int moe_pack_expert_weights(const moe_cfg* cfg, const void* w1, const void* w2,

@@ -314,6 +314,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
       src[lane] = i / K;
     }
   }
+  if (!xd) return;  // routing metadata only (uniform)
   __syncthreads();
   copy_rows<SBR, 8>(x, xd, dst, src, row_vecs, q_scale);
 }
@@ -337,6 +338,32 @@ __global__ __launch_bounds__(256) void gather_bytes_kernel(const uint8_t* __rest
 size_t dispatch_ws_bytes(int64_t A, int E) {
   const int64_t nb = (A + RPB - 1) / RPB;
   return align_up((size_t)(nb > 0 ? nb : 1) * (size_t)(E + 1) * sizeof(int32_t), 256);
+}
+
+static hipError_t gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
+                              int E, int64_t row_bytes, int64_t r_max, void* dst, hipStream_t s,
+                              const float* q_scale) {
+  if (r_max == 0) return hipSuccess;
+  const bool vec = row_bytes % 16 == 0 && ((uintptr_t)x & 15u) == 0 &&
+                   ((uintptr_t)dst & 15u) == 0;
+  if (q_scale && !vec) return hipErrorInvalidValue;
+  if (vec) {
+    constexpr int ROWS = 16;
+    const int64_t grid = (r_max + ROWS - 1) / ROWS;
+    hipLaunchKernelGGL((gather_kernel<ROWS>), dim3((unsigned)grid), dim3(256), 0, s,
+                       (const u32x4*)x, row_token, offsets, E, (int)(row_bytes / 16), dst,
+                       q_scale);
+  } else {
+    hipLaunchKernelGGL(gather_bytes_kernel, dim3((unsigned)r_max), dim3(256), 0, s,
+                       (const uint8_t*)x, row_token, offsets, E, row_bytes, (uint8_t*)dst);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
+                              int E, int64_t row_bytes, int64_t r_max, void* dst,
+                              hipStream_t s) {
+  return gather_rows(x, row_token, offsets, E, row_bytes, r_max, dst, s, nullptr);
 }
 
 hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int64_t A, int K, int E,
@@ -365,19 +392,8 @@ hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int64_t A, in
   hipLaunchKernelGGL(slot_kernel, dim3(nb > 0 ? nb : 1), dim3(256), 0, s, topk_idx, A, K, E,
                      cap, nb, counts, offsets, route_rank, route_row, row_token, load);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || r_max == 0) return err;
-  if (vec) {
-    constexpr int ROWS = 16;
-    const int64_t grid = (r_max + ROWS - 1) / ROWS;
-    hipLaunchKernelGGL((gather_kernel<ROWS>), dim3((unsigned)grid), dim3(256), 0, s,
-                       (const u32x4*)x, row_token, offsets, E, (int)(row_bytes / 16), x_disp,
-                       q_scale);
-  } else {
-    hipLaunchKernelGGL(gather_bytes_kernel, dim3((unsigned)r_max), dim3(256), 0, s,
-                       (const uint8_t*)x, row_token, offsets, E, row_bytes,
-                       (uint8_t*)x_disp);
-  }
-  return hipGetLastError();
+  if (err != hipSuccess || r_max == 0 || !x_disp) return err;
+  return gather_rows(x, row_token, offsets, E, row_bytes, r_max, x_disp, s, q_scale);
 }
 
 }  // namespace moe

@@ -196,11 +196,14 @@ struct StreamShape {
 // (rows <= BM), so tile L is (expert L / (N/BN), weight tile L % (N/BN)) with
 // no look at `offsets`: the weight prefetch is issued before the expert's row
 // range arrives, and a workgroup of an empty expert leaves after reading it.
+// rowmap != nullptr: activation row r is A[rowmap[r]] (the dispatch gather,
+// done by the loads themselves: A is then the token matrix x).
 template <int MT, int WN, int WK, int EPI, bool PK, int OCC>
 __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, void* __restrict__ out,
-    const int32_t* __restrict__ offsets, int E, int N, int Kd, int one_rt) {
+    const int32_t* __restrict__ offsets, int E, int N, int Kd, int one_rt,
+    const int32_t* __restrict__ rowmap) {
   using S = StreamShape<MT, WN, WK, OCC>;
   static_assert(S::PD % S::AD == 0 && S::PD % 2 == 0, "ring sizes");
   // the epilogue stages all BM output rows at once when they fit in 48 KB
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     const int c = tid + 256 * j;
     const int r = c >> 3, q = c & 7;
     const int row = min(row0 + r, row_end - 1);
-    ap[j] = A + (size_t)row * Kd + q * 8;
+    ap[j] = A + (size_t)(rowmap ? rowmap[row] : row) * Kd + q * 8;
     alds[j] = act_slot(r, q);
   }
   // activation fragments: the quad of the chunk that matches the weights' k
@@ -851,43 +854,45 @@ int64_t grid_for(int64_t r_max, int BM, int E, int N, int BN) {
 template <int MT, int WN, int WK, int EPI, bool PK, int OCC>
 hipError_t launch_stream(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
                          const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
-                         bool static_map, hipStream_t s) {
+                         bool static_map, const int32_t* rowmap, hipStream_t s) {
   // static_map: every expert's rows fit one row tile (see the kernel)
   const int one_rt = static_map ? 1 : 0;
   const int64_t grid = one_rt ? ((int64_t)E * (N / (32 * WN)) + NXCD - 1) / NXCD * NXCD
                               : grid_for(r_max, 32 * MT, E, N, 32 * WN);
   hipLaunchKernelGGL((stream_gemm_kernel<MT, WN, WK, EPI, PK, OCC>), dim3((unsigned)grid),
-                     dim3(256), 0, s, A, W, bias, out, offsets, E, N, Kd, one_rt);
+                     dim3(256), 0, s, A, W, bias, out, offsets, E, N, Kd, one_rt, rowmap);
   return hipGetLastError();
 }
 
 template <int MT, int WN, int WK, int EPI, bool PK>
 hipError_t launch_stream_occ(bool occ1, const uint16_t* A, const uint16_t* W, const float* bias,
                              void* out, const int32_t* offsets, int E, int N, int Kd,
-                             int64_t r_max, bool static_map, hipStream_t s) {
+                             int64_t r_max, bool static_map, const int32_t* rowmap,
+                             hipStream_t s) {
   // built only for the tall tiles, where one workgroup per CU is the common case
   if constexpr (MT >= 4 && WN == 2)
     if (occ1)
       return launch_stream<MT, WN, WK, EPI, PK, 1>(A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                   static_map, s);
+                                                   static_map, rowmap, s);
   return launch_stream<MT, WN, WK, EPI, PK, 2>(A, W, bias, out, offsets, E, N, Kd, r_max,
-                                               static_map, s);
+                                               static_map, rowmap, s);
 }
 
 template <int MT, int EPI, bool PK>
 hipError_t launch_stream_mt(int wn, bool occ1, const uint16_t* A, const uint16_t* W,
                             const float* bias, void* out, const int32_t* offsets, int E, int N,
-                            int Kd, int64_t r_max, bool static_map, hipStream_t s) {
+                            int Kd, int64_t r_max, bool static_map, const int32_t* rowmap,
+                            hipStream_t s) {
   if (wn == 4)
     return launch_stream_occ<MT, 4, 1, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                static_map, s);
+                                                static_map, rowmap, s);
   // the 4-way k split keeps MT <= 3 (its reduction and ring outgrow the registers)
   if (wn == 2 || MT >= 4)
     return launch_stream_occ<MT, 2, 2, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                static_map, s);
+                                                static_map, rowmap, s);
   if constexpr (MT < 4)
     return launch_stream_occ<MT, 1, 4, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                static_map, s);
+                                                static_map, rowmap, s);
   return hipErrorInvalidValue;
 }
 
@@ -923,11 +928,19 @@ hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const float* bias,
 //    rows_max <= 160 (each weight byte read once), else 128-row tiles; the
 //    weight-tile width 32*WN is the widest that still gives >= 256
 //    workgroups (one per CU), narrower ones split the k-chunk across waves.
+// Whether launch_gemm_auto takes the streaming shape (the only one whose
+// loads can gather activation rows through a row map).
+bool takes_stream_shape(bool first, int N, int64_t rows_typ) {
+  if (rows_typ >= 512 && N % 256 == 0 && first) return false;
+  return rows_typ < 384;
+}
+
 template <int EPI, bool PK>
 hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* bias,
                             void* out, const int32_t* offsets, int E, int N, int Kd,
                             int64_t r_max, int64_t rows_typ, int64_t rows_max,
-                            hipStream_t s) {
+                            const int32_t* rowmap, hipStream_t s) {
+  if (rowmap && !takes_stream_shape(EPI == 0, N, rows_typ)) return hipErrorInvalidValue;
   if (rows_typ >= 512 && N % 256 == 0 && EPI == 0)
     return launch_wide<256, 256, EPI, PK, 1>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
   if (rows_typ >= 384 && N % 128 == 0)
@@ -951,7 +964,7 @@ hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* b
   switch (mt) {
 #define MOE_MT_CASE(M_)                                                                    \
     return launch_stream_mt<M_, EPI, PK>(wn, occ1, A, W, bias, out, offsets, E, N, Kd, r_max, \
-                                         one_rt, s)
+                                         one_rt, rowmap, s)
     case 1: MOE_MT_CASE(1);
     case 2: MOE_MT_CASE(2);
     case 3: MOE_MT_CASE(3);
@@ -961,33 +974,44 @@ hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* b
   }
 }
 
+// row_token != nullptr: xd is the token matrix x and row r's activations are
+// x[row_token[r]].  The streaming shape gathers them in its loads; the other
+// shapes first copy the rows into y's storage (R_max rows of h bf16 fit in
+// the R_max x h fp32 of y), which GEMM1 reads before GEMM2 overwrites it.
 template <bool PK>
-hipError_t launch_ffn_bf16_t(const uint16_t* xd, const int32_t* offsets, const uint16_t* w1,
-                             const float* b1, const uint16_t* w2, const float* b2,
-                             uint16_t* hbuf, float* y, int E, int h, int F, int64_t A,
-                             int64_t cap, int64_t r_max, hipStream_t s) {
+hipError_t launch_ffn_bf16_t(const uint16_t* xd, const int32_t* row_token,
+                             const int32_t* offsets, const uint16_t* w1, const float* b1,
+                             const uint16_t* w2, const float* b2, uint16_t* hbuf, float* y,
+                             int E, int h, int F, int64_t A, int64_t cap, int64_t r_max,
+                             hipStream_t s) {
   if (r_max == 0) return hipSuccess;
   const int64_t avg = (A + E - 1) / E;
   const int64_t rows_typ = avg < cap ? avg : cap;
   const int64_t rows_max = A < cap ? A : cap;
+  if (row_token && !takes_stream_shape(true, F, rows_typ)) {
+    hipError_t err = launch_gather_rows(xd, row_token, offsets, E, (int64_t)h * 2, r_max, y, s);
+    if (err != hipSuccess) return err;
+    xd = (const uint16_t*)y;
+    row_token = nullptr;
+  }
   hipError_t err = launch_gemm_auto<0, PK>(xd, w1, b1, hbuf, offsets, E, F, h, r_max, rows_typ,
-                                           rows_max, s);
+                                           rows_max, row_token, s);
   if (err != hipSuccess) return err;
   return launch_gemm_auto<1, PK>(hbuf, w2, b2, y, offsets, E, h, F, r_max, rows_typ, rows_max,
-                                 s);
+                                 nullptr, s);
 }
 
 }  // namespace
 
-hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* offsets, const uint16_t* w1,
-                           const float* b1, const uint16_t* w2, const float* b2,
-                           uint16_t* hbuf, float* y, int E, int h, int F, int64_t A,
-                           int64_t cap, int64_t r_max, bool packed, hipStream_t s) {
+hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* row_token, const int32_t* offsets,
+                           const uint16_t* w1, const float* b1, const uint16_t* w2,
+                           const float* b2, uint16_t* hbuf, float* y, int E, int h, int F,
+                           int64_t A, int64_t cap, int64_t r_max, bool packed, hipStream_t s) {
   if (packed)
-    return launch_ffn_bf16_t<true>(xd, offsets, w1, b1, w2, b2, hbuf, y, E, h, F, A, cap,
-                                   r_max, s);
-  return launch_ffn_bf16_t<false>(xd, offsets, w1, b1, w2, b2, hbuf, y, E, h, F, A, cap, r_max,
-                                  s);
+    return launch_ffn_bf16_t<true>(xd, row_token, offsets, w1, b1, w2, b2, hbuf, y, E, h, F, A,
+                                   cap, r_max, s);
+  return launch_ffn_bf16_t<false>(xd, row_token, offsets, w1, b1, w2, b2, hbuf, y, E, h, F, A,
+                                  cap, r_max, s);
 }
 
 hipError_t launch_pack_weights(const uint16_t* w, uint16_t* wp, int E, int N, int Kd,
@@ -999,10 +1023,16 @@ hipError_t launch_pack_weights(const uint16_t* w, uint16_t* wp, int E, int N, in
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_f32(const float* xd, const int32_t* offsets, const float* w1,
-                          const float* b1, const float* w2, const float* b2, float* hbuf,
-                          float* y, int E, int h, int F, int64_t r_max, hipStream_t s) {
+hipError_t launch_ffn_f32(const float* xd, const int32_t* row_token, const int32_t* offsets,
+                          const float* w1, const float* b1, const float* w2, const float* b2,
+                          float* hbuf, float* y, int E, int h, int F, int64_t r_max,
+                          hipStream_t s) {
   if (r_max == 0) return hipSuccess;
+  if (row_token) {  // rows of x into y's storage first (read before GEMM2 writes y)
+    hipError_t err = launch_gather_rows(xd, row_token, offsets, E, (int64_t)h * 4, r_max, y, s);
+    if (err != hipSuccess) return err;
+    xd = y;
+  }
   int64_t n1 = r_max * F, n2 = r_max * h;
   hipLaunchKernelGGL((ffn_f32_kernel<0>), dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0,
                      s, xd, w1, b1, hbuf, offsets, E, F, h, r_max);

@@ -176,8 +176,14 @@ __device__ __forceinline__ uint2 quantize8(u32x4 v, float scale) {
   return make_uint2(out[0], out[1]);
 }
 
+// dst[row] = x[row_token[row]] for row < offsets[E] (rows of row_bytes bytes;
+// r_max bounds offsets[E]).
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* offsets,
+                              int E, int64_t row_bytes, int64_t r_max, void* dst,
+                              hipStream_t s);
 // q_scale: NULL for a plain row copy, else the device address of the FP8
-// scale; then x holds bf16 rows and x_disp receives E4M3 codes (h bytes/row)
+// scale; then x holds bf16 rows and x_disp receives E4M3 codes (h bytes/row).
+// x_disp == NULL: routing metadata only, no row is copied.
 hipError_t launch_dispatch(const void* x, const int32_t* topk_idx, int64_t A, int K, int E,
                            int64_t cap, int64_t row_bytes, int64_t r_max,
                            int32_t* offsets, int32_t* route_rank, int32_t* route_row,
@@ -191,16 +197,20 @@ hipError_t launch_fp8_scale(const uint16_t* x, int64_t n, float* scale, void* ws
 hipError_t launch_fp8_dequantize(const uint8_t* xq, const float* scale, const int32_t* offsets,
                                  int E, int h, int64_t r_max, uint16_t* x_disp, hipStream_t s);
 
-hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* offsets, const uint16_t* w1,
-                           const float* b1, const uint16_t* w2, const float* b2,
-                           uint16_t* hbuf, float* y, int E, int h, int F, int64_t A,
-                           int64_t cap, int64_t r_max, bool packed, hipStream_t s);
+// row_token == nullptr: xd holds the dispatched rows; else xd is the token
+// matrix x and row r reads x[row_token[r]] (y's storage may serve as the
+// staging buffer of that gather).
+hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* row_token, const int32_t* offsets,
+                           const uint16_t* w1, const float* b1, const uint16_t* w2,
+                           const float* b2, uint16_t* hbuf, float* y, int E, int h, int F,
+                           int64_t A, int64_t cap, int64_t r_max, bool packed, hipStream_t s);
 // Row-major [E, N, K] bf16 -> packed fragment blocks (N % 32 == 0, K % 64 == 0).
 hipError_t launch_pack_weights(const uint16_t* w, uint16_t* wp, int E, int N, int Kd,
                                hipStream_t s);
-hipError_t launch_ffn_f32(const float* xd, const int32_t* offsets, const float* w1,
-                          const float* b1, const float* w2, const float* b2, float* hbuf,
-                          float* y, int E, int h, int F, int64_t r_max, hipStream_t s);
+hipError_t launch_ffn_f32(const float* xd, const int32_t* row_token, const int32_t* offsets,
+                          const float* w1, const float* b1, const float* w2, const float* b2,
+                          float* hbuf, float* y, int E, int h, int F, int64_t r_max,
+                          hipStream_t s);
 
 hipError_t launch_combine(const float* y, const int32_t* route_row, const float* gate,
                           float* out, int T, int K, int h, hipStream_t s);

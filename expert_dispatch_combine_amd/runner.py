@@ -101,7 +101,9 @@ class LayerPlan:
     marshalled once.  `launch()` enqueues it with bare C calls; the ledger
     runs on `side` (after the dispatch, beside the FFN) when given, joined back
     into `main` before launch() returns; with fused_tail it runs with the
-    combine in one moe_combine_ledger call.  After the work has completed,
+    combine in one moe_combine_ledger call.  gather_in_ffn: moe_dispatch
+    moves no row and moe_expert_ffn_rows reads x[row_token[r]] itself (b.x_disp
+    is then left untouched).  After the work has completed,
     `ledger()` decodes the stage on the host.
 
     The plan does not own the tensors: they must outlive it and keep their
@@ -112,7 +114,7 @@ class LayerPlan:
     def __init__(self, b: LayerBuffers, x, w_gate, logit_bias, w1, b1, w2, b2, src_rank,
                  owner_rank, n_ep: int, alpha: float = 0.01, main=None, side=None,
                  ledger_ws=None, packed: bool = False, logits_in: bool = False,
-                 fused_tail: bool = False):
+                 fused_tail: bool = False, gather_in_ffn: bool = False):
         lib = load_library()
         cfg = b.cfg
         self.b, self.cfg, self.n_ep, self.alpha = b, cfg, int(n_ep), float(alpha)
@@ -140,19 +142,23 @@ class LayerPlan:
                                       p(b.logits, "f32", "logits"),
                                       p(b.topk_idx, "i32", "topk_idx"),
                                       p(b.topk_gate, "f32", "topk_gate"), None, wsp, wsb, ms))
+        xd = None if gather_in_ffn else p(b.x_disp, "act", "x_disp")
         self.dispatch = (lib.moe_dispatch, (c, p(x, "act", "x"), p(b.topk_idx, "i32", "topk_idx"),
                                             b.capacity, p(b.expert_offsets, "i32", "offsets"),
                                             p(b.route_rank, "i32", "route_rank"),
                                             p(b.route_row, "i32", "route_row"),
-                                            p(b.row_token, "i32", "row_token"),
-                                            p(b.x_disp, "act", "x_disp"),
+                                            p(b.row_token, "i32", "row_token"), xd,
                                             p(b.expert_load, "i32", "expert_load"), wsp, wsb, ms))
-        ffn_fn = lib.moe_expert_ffn_packed if packed else lib.moe_expert_ffn
-        self.ffn = (ffn_fn, (c, b.capacity, p(b.x_disp, "act", "x_disp"),
-                                         p(b.expert_offsets, "i32", "offsets"),
-                                         p(w1, "act", "w1"), p(b1, "f32", "b1"),
-                                         p(w2, "act", "w2"), p(b2, "f32", "b2"),
-                                         p(b.h_buf, "act", "h_buf"), p(b.y, "f32", "y"), ms))
+        wargs = (p(b.expert_offsets, "i32", "offsets"), p(w1, "act", "w1"), p(b1, "f32", "b1"),
+                 p(w2, "act", "w2"), p(b2, "f32", "b2"), p(b.h_buf, "act", "h_buf"),
+                 p(b.y, "f32", "y"))
+        if gather_in_ffn:  # the FFN's loads gather x[row_token[r]]; no x_disp
+            self.ffn = (lib.moe_expert_ffn_rows, (c, b.capacity, p(x, "act", "x"),
+                                                  p(b.row_token, "i32", "row_token"), *wargs,
+                                                  int(bool(packed)), ms))
+        else:
+            ffn_fn = lib.moe_expert_ffn_packed if packed else lib.moe_expert_ffn
+            self.ffn = (ffn_fn, (c, b.capacity, p(b.x_disp, "act", "x_disp"), *wargs, ms))
         self.combine = (lib.moe_combine, (c, p(b.y, "f32", "y"), p(b.route_row, "i32", "route_row"),
                                           p(b.topk_gate, "f32", "topk_gate"),
                                           p(b.out, "f32", "out"), ms))

@@ -188,7 +188,9 @@ int moe_bias_update(const moe_cfg* cfg, const int32_t* topk_idx, float* expert_b
  *   route_row      [T,K] int32   offset[e] + rank if rank < capacity, else -1
  *   row_token      [R_max] int32 token of each accepted row (rows >= R are
  *                                left untouched)
- *   x_disp         [R_max, h] dtype  x_disp[row] = x[row_token[row]]
+ *   x_disp         [R_max, h] dtype  x_disp[row] = x[row_token[row]]; or NULL:
+ *                                    routing metadata only (x may then be
+ *                                    NULL), for moe_expert_ffn_rows
  *   expert_load    [E] int32|NULL    pre-capacity load of each expert
  * ws: at least moe_workspace_bytes(cfg) bytes.
  * Dropless variant: any capacity >= T accepts every route (a token's K
@@ -235,6 +237,20 @@ int moe_expert_ffn_packed(const moe_cfg* cfg, int64_t capacity, const void* x_di
  * Output buffers must not alias the inputs.  Asynchronous on `stream`. */
 int moe_pack_expert_weights(const moe_cfg* cfg, const void* w1, const void* w2,
                             void* w1_packed, void* w2_packed, void* stream);
+
+/* The expert FFN reading its rows from the token matrix: the same H and Y as
+ * moe_expert_ffn (packed == 0) or moe_expert_ffn_packed (packed != 0) on
+ * x_disp[r] = x[row_token[r]] ([EPC] Dispatch; [DSV3] section 一 FFN), with
+ * that gather done by the first GEMM's own loads where its rows are few (a
+ * few hundred per expert or less), and otherwise by a row copy into y's
+ * storage that the first GEMM reads before the second writes y.  Pairs with
+ * moe_dispatch(x_disp = NULL), which then moves no row.
+ *   x [T, h] dtype (16-byte aligned); row_token [R_max] int32 from
+ *   moe_dispatch; the other arguments as for moe_expert_ffn. */
+int moe_expert_ffn_rows(const moe_cfg* cfg, int64_t capacity, const void* x,
+                        const int32_t* row_token, const int32_t* expert_offsets,
+                        const void* w1, const float* b1, const void* w2, const float* b2,
+                        void* h_buf, float* y, int32_t packed, void* stream);
 
 /* Weighted combine in original token order, without atomics ([EP46]
  * combine_expert_outputs; [EPC] Combine):

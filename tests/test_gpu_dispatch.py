@@ -56,6 +56,34 @@ def test_dispatch_on_workloads(cid):
     _check(cfg, inp.x, idx, cap)
 
 
+@pytest.mark.parametrize("T,E,K,cf,dtype", [(2048, 16, 1, 1.25, "bf16"), (9000, 64, 2, 1.0, "bf16"),
+                                            (300, 5, 2, 0.7, "f32")])
+def test_dispatch_metadata_only(T, E, K, cf, dtype):
+    """x_disp = NULL (and x = NULL): the same offsets, ranks, rows, row_token and
+    loads, no row moved -- the one-launch path (<= 8192 routes) and the
+    three-kernel path."""
+    banner(f"dispatch metadata only T={T} E={E} K={K}")
+    rng = np.random.default_rng(T + E)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    cfg = W.custom(T=T, h=64, E=E, K=K, F=64, cf=cf, dtype=dtype)
+    cap = O.capacity(T * K, E, cf)
+    sl = O.slot_routes(idx, E, cap)
+    mc = M.MoeCfg.make(T, 64, E, K, 64, dtype, cf)
+    b = LayerBuffers(mc, cap)
+    b.topk_idx.copy_(torch.from_numpy(idx))
+    b.row_token.fill_(-7)
+    sentinel = b.x_disp.view(torch.uint8).fill_(0x5A).clone()
+    M.moe_dispatch(mc, None, b.topk_idx, cap, b.expert_offsets, b.route_rank, b.route_row,
+                   b.row_token, None, b.expert_load, b.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(b.expert_offsets.cpu().numpy(), sl["expert_offsets"])
+    assert np.array_equal(b.route_rank.cpu().numpy(), sl["route_rank"])
+    assert np.array_equal(b.route_row.cpu().numpy(), sl["route_row"])
+    assert np.array_equal(b.row_token.cpu().numpy()[:sl["R"]], sl["row_token"])
+    assert np.array_equal(b.expert_load.cpu().numpy().astype(np.int64), O.expert_loads(idx, E))
+    assert torch.equal(b.x_disp.view(torch.uint8), sentinel)
+
+
 def _random_idx(rng, T, E, K):
     return np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32) if T else \
         np.zeros((0, K), np.int32)

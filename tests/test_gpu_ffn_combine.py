@@ -163,6 +163,42 @@ def test_ffn_ragged_segments(T, h, E, K, F, cf, packed):
     _check_rows(inp, sl, b, np.arange(sl["R"]))
 
 
+@pytest.mark.parametrize("cid,shape,packed", [
+    (2, None, True), (2, None, False),                     # gather in the streaming loads
+    (None, (2048, 768, 14, 1, 3072, 1.0), True),           # ragged, static tile map
+    (None, (1000, 256, 4, 1, 320, 1.0), False),            # 250-row experts: tile search
+    (None, (513, 64, 64, 6, 128, 1.0), True),              # many small / empty experts
+    (None, (2500, 192, 3, 1, 448, 1.5), True),             # long segments: copy into y first
+    (None, (1, 64, 1, 1, 64, 1.0), False),
+    (1, None, False)])                                      # fp32: copy into y first
+def test_ffn_rows_equals_ffn_on_x_disp(cid, shape, packed):
+    """moe_expert_ffn_rows on x and row_token gives the same H and Y, bit for
+    bit, as moe_expert_ffn(_packed) on x_disp[r] = x[row_token[r]]."""
+    banner(f"ffn rows cid={cid} shape={shape} packed={packed}")
+    if cid is not None:
+        inp = device_inputs(cid)
+    else:
+        T, h, E, K, F, cf = shape
+        inp = custom_inputs(W.custom(T=T, h=h, E=E, K=K, F=F, cf=cf, dtype="bf16",
+                                     seed=T * 3 + F))
+    _, _, cap, sl = _oracle_dispatch(inp)
+    ref = _run_ffn(inp, cap, sl, packed)
+    cfg = inp.cfg
+    mc = M.MoeCfg.make(cfg.T, cfg.h, cfg.E, cfg.K, cfg.F, cfg.dtype, cfg.cf)
+    b = LayerBuffers(mc, cap)
+    R = sl["R"]
+    b.row_token.fill_(-7)
+    if R:
+        b.row_token[:R].copy_(torch.from_numpy(sl["row_token"].astype(np.int32)))
+    b.expert_offsets.copy_(torch.from_numpy(sl["expert_offsets"]))
+    w1, w2 = (pack_weights(mc, inp.w1, inp.w2) if packed else (inp.w1, inp.w2))
+    M.moe_expert_ffn_rows(mc, cap, inp.x, b.row_token, b.expert_offsets, w1, inp.b1, w2, inp.b2,
+                          b.h_buf, b.y, packed)
+    torch.cuda.synchronize()
+    assert torch.equal(b.h_buf[:R], ref.h_buf[:R])
+    assert torch.equal(b.y[:R], ref.y[:R])
+
+
 def test_ffn_fp32_odd_sizes():
     banner("ffn fp32 odd sizes")
     cfg = W.custom(T=50, h=7, E=3, K=2, F=5, cf=1.0, dtype="f32", seed=4)

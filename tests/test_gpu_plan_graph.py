@@ -28,16 +28,18 @@ def _same(a, c):
     assert a["acc"] == c["acc"] and a["P"] == c["P"] and a["loads"] == c["loads"]
 
 
-@pytest.mark.parametrize("cid,packed,tail", [(1, False, "side"), (2, False, "side"),
-                                             (2, True, "side"), (3, True, "side"),
-                                             (4, True, "side"), (5, True, "side"),
-                                             (1, False, "fused"), (2, True, "fused"),
-                                             (5, True, "fused")])
-def test_plan_and_graph_replay_match_eager(cid, packed, tail):
+@pytest.mark.parametrize("cid,packed,tail,gather", [
+    (1, False, "side", False), (2, False, "side", False), (2, True, "side", False),
+    (3, True, "side", False), (4, True, "side", False), (5, True, "side", False),
+    (1, False, "fused", True), (2, True, "fused", True), (4, True, "fused", True),
+    (5, True, "fused", True)])
+def test_plan_and_graph_replay_match_eager(cid, packed, tail, gather):
     """tail "side": the ledger on a second stream beside the FFN; "fused":
     combine and ledger in one moe_combine_ledger call (one launch for
-    workloads 1 and 2, two for workload 5's 98304 routes)."""
-    banner(f"plan/graph config {cid} packed={packed} tail={tail}")
+    workloads 1 and 2, two for workload 5's 98304 routes).  gather: the
+    dispatch moves no row and moe_expert_ffn_rows gathers them (in the first
+    GEMM's loads for workloads 2 and 4, by a copy into y first for 1 and 5)."""
+    banner(f"plan/graph config {cid} packed={packed} tail={tail} gather={gather}")
     inp = device_inputs(cid)
     cfg = inp.cfg
     b = buffers_for(cfg)
@@ -52,7 +54,7 @@ def test_plan_and_graph_replay_match_eager(cid, packed, tail):
     main, side = torch.cuda.Stream(), torch.cuda.Stream()
     plan = LayerPlan(b, *args, inp.src_rank, inp.owner_rank, cfg.n_ep, main=main,
                      side=side if tail == "side" else None, packed=packed,
-                     fused_tail=tail == "fused")
+                     fused_tail=tail == "fused", gather_in_ffn=gather)
     b.out.zero_()
     with torch.cuda.stream(main):
         plan.launch()
