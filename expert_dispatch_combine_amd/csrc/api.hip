@@ -209,10 +209,11 @@ static int expert_ffn_common(const moe_cfg* cfg, int64_t capacity, const void* x
     if (!aligned16(x_disp) || !aligned16(w1) || !aligned16(w2) || !aligned16(h_buf) ||
         !aligned16(y) || !aligned16(b1) || !aligned16(b2))
       return MOE_ERR_INVALID_ARG;
-    return hip_status(launch_ffn_bf16((const uint16_t*)x_disp, row_token, expert_offsets,
-                                      (const uint16_t*)w1, b1, (const uint16_t*)w2, b2,
-                                      (uint16_t*)h_buf, y, cfg->E, cfg->h, cfg->F,
-                                      routes_of(cfg), capacity, rmax, packed, s));
+    return hip_status(launch_ffn_bf16((const uint16_t*)x_disp, row_token, cfg->T,
+                                      expert_offsets, (const uint16_t*)w1, b1,
+                                      (const uint16_t*)w2, b2, (uint16_t*)h_buf, y, cfg->E,
+                                      cfg->h, cfg->F, routes_of(cfg), capacity, rmax, packed,
+                                      s));
   }
   return hip_status(launch_ffn_f32((const float*)x_disp, row_token, expert_offsets,
                                    (const float*)w1, b1, (const float*)w2, b2, (float*)h_buf, y,

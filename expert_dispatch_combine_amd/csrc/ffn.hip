@@ -476,7 +476,8 @@ template <int BN, int EPI, bool PK>
 __global__ __launch_bounds__(256, 2) void tiled_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, void* __restrict__ out,
-    const int32_t* __restrict__ offsets, int E, int N, int Kd) {
+    const int32_t* __restrict__ offsets, int E, int N, int Kd,
+    const int32_t* __restrict__ rowmap) {
   constexpr int TM = 2;        // 32-row MFMA tiles per wave (wave covers 64 rows)
   constexpr int TN = BN / 64;  // 32-col MFMA tiles per wave (wave covers BN/2 cols)
   constexpr int ACH = TBM * TBK / 8 / 256;  // 16-byte chunks per thread per stage (A)
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(256, 2) void tiled_gemm_kernel(
     const int c = tid + j * 256;
     const int r = c >> 3, cc = c & 7;
     const int row = min(row0 + r, row_end - 1);
-    a_src[j] = A + (size_t)row * Kd + cc * 8;
+    a_src[j] = A + (size_t)(rowmap ? rowmap[row] : row) * Kd + cc * 8;
     a_lds[j] = r * TLDS + cc * 8;
   }
   // weight staging: row-major -> 16-byte chunk (row c/8, quad c%8) of the
@@ -616,7 +617,8 @@ template <int WBM, int BN, int EPI, bool PK, int OCC>
 __global__ __launch_bounds__(256, OCC) void wide_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, void* __restrict__ out,
-    const int32_t* __restrict__ offsets, int E, int N, int Kd) {
+    const int32_t* __restrict__ offsets, int E, int N, int Kd,
+    const int32_t* __restrict__ rowmap) {
   constexpr int TM = WBM / 64;         // 32-row MFMA tiles per wave
   constexpr int TN = BN / 64;          // 32-column MFMA tiles per wave
   constexpr int AQ = WBM * 8 / 256;    // 16-byte quads per thread and chunk: activations
@@ -640,15 +642,20 @@ __global__ __launch_bounds__(256, OCC) void wide_gemm_kernel(
   // linearly).  Sources are 32-bit element offsets from per-tile bases;
   // chunk c adds c * 64 (activations, row-major weights) or c * PBLK.  The
   // swizzle of row r + 32 j equals that of r, so LDS slots step by 32 rows.
-  const uint16_t* abase = A + (size_t)row0 * Kd;
+  // rowmap: the base is the token matrix and the offsets name token rows (the
+  // host keeps its element count below 2^32)
+  const uint16_t* abase = rowmap ? A : A + (size_t)row0 * Kd;
   const uint16_t* wbase = PK ? W + ((size_t)e * (N / 32) + n0 / 32) * nk * PBLK
                              : W + ((size_t)e * N + n0) * Kd;
   const int sr = tid >> 3, sq = tid & 7;
   // (unsigned, so that the loads take a scalar base plus a 32-bit offset)
   uint32_t aoff[AQ];
 #pragma unroll
-  for (int j = 0; j < AQ; ++j)
-    aoff[j] = (uint32_t)((min(row0 + sr + 32 * j, row_end - 1) - row0) * Kd + sq * 8);
+  for (int j = 0; j < AQ; ++j) {
+    const int row = min(row0 + sr + 32 * j, row_end - 1);
+    aoff[j] = rowmap ? (uint32_t)rowmap[row] * (uint32_t)Kd + sq * 8
+                     : (uint32_t)((row - row0) * Kd + sq * 8);
+  }
   const uint32_t woff0 = PK ? tid * 8 : sr * Kd + sq * 8;
   const uint32_t wjstr = PK ? nk * PBLK : 32 * Kd;  // next quad of this thread
   const int adst = act_slot(sr, sq);
@@ -899,20 +906,20 @@ hipError_t launch_stream_mt(int wn, bool occ1, const uint16_t* A, const uint16_t
 template <int WBM, int BN, int EPI, bool PK, int OCC>
 hipError_t launch_wide(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
                        const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
-                       hipStream_t s) {
+                       const int32_t* rowmap, hipStream_t s) {
   const int64_t grid = grid_for(r_max, WBM, E, N, BN);
   hipLaunchKernelGGL((wide_gemm_kernel<WBM, BN, EPI, PK, OCC>), dim3((unsigned)grid), dim3(256),
-                     0, s, A, W, bias, out, offsets, E, N, Kd);
+                     0, s, A, W, bias, out, offsets, E, N, Kd, rowmap);
   return hipGetLastError();
 }
 
 template <int BN, int EPI, bool PK>
 hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
                         const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
-                        hipStream_t s) {
+                        const int32_t* rowmap, hipStream_t s) {
   const int64_t grid = grid_for(r_max, TBM, E, N, BN);
   hipLaunchKernelGGL((tiled_gemm_kernel<BN, EPI, PK>), dim3((unsigned)grid), dim3(256), 0, s,
-                     A, W, bias, out, offsets, E, N, Kd);
+                     A, W, bias, out, offsets, E, N, Kd, rowmap);
   return hipGetLastError();
 }
 
@@ -928,11 +935,10 @@ hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const float* bias,
 //    rows_max <= 160 (each weight byte read once), else 128-row tiles; the
 //    weight-tile width 32*WN is the widest that still gives >= 256
 //    workgroups (one per CU), narrower ones split the k-chunk across waves.
-// Whether launch_gemm_auto takes the streaming shape (the only one whose
-// loads can gather activation rows through a row map).
-bool takes_stream_shape(bool first, int N, int64_t rows_typ) {
-  if (rows_typ >= 512 && N % 256 == 0 && first) return false;
-  return rows_typ < 384;
+// Whether launch_gemm_auto takes the wide shape, whose loads address
+// activations by 32-bit element offsets.
+bool takes_wide_shape(bool first, int N, int64_t rows_typ) {
+  return (rows_typ >= 512 && N % 256 == 0 && first) || (rows_typ >= 384 && N % 128 == 0);
 }
 
 template <int EPI, bool PK>
@@ -940,13 +946,15 @@ hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* b
                             void* out, const int32_t* offsets, int E, int N, int Kd,
                             int64_t r_max, int64_t rows_typ, int64_t rows_max,
                             const int32_t* rowmap, hipStream_t s) {
-  if (rowmap && !takes_stream_shape(EPI == 0, N, rows_typ)) return hipErrorInvalidValue;
-  if (rows_typ >= 512 && N % 256 == 0 && EPI == 0)
-    return launch_wide<256, 256, EPI, PK, 1>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+  if constexpr (EPI == 0)  // the 256 x 256 tiles serve the first GEMM only
+    if (rows_typ >= 512 && N % 256 == 0)
+      return launch_wide<256, 256, EPI, PK, 1>(A, W, bias, out, offsets, E, N, Kd, r_max,
+                                               rowmap, s);
   if (rows_typ >= 384 && N % 128 == 0)
-    return launch_wide<128, 128, EPI, PK, 2>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+    return launch_wide<128, 128, EPI, PK, 2>(A, W, bias, out, offsets, E, N, Kd, r_max, rowmap,
+                                             s);
   if (rows_typ >= 384)
-    return launch_tiled<64, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, s);
+    return launch_tiled<64, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, rowmap, s);
   int mt = (int)((rows_max + 31) / 32);
   if (mt > 5) mt = 4;
   if (mt < 1) mt = 1;
@@ -974,12 +982,14 @@ hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* b
   }
 }
 
-// row_token != nullptr: xd is the token matrix x and row r's activations are
-// x[row_token[r]].  The streaming shape gathers them in its loads; the other
-// shapes first copy the rows into y's storage (R_max rows of h bf16 fit in
-// the R_max x h fp32 of y), which GEMM1 reads before GEMM2 overwrites it.
+// row_token != nullptr: xd is the token matrix x (x_rows rows) and row r's
+// activations are x[row_token[r]].  GEMM1 gathers them in its own loads,
+// except in the wide shape when x holds 2^32 elements or more (its loads
+// take 32-bit offsets): then the rows are first copied into y's storage
+// (R_max rows of h bf16 fit in the R_max x h fp32 of y), which GEMM1 reads
+// before GEMM2 overwrites it.
 template <bool PK>
-hipError_t launch_ffn_bf16_t(const uint16_t* xd, const int32_t* row_token,
+hipError_t launch_ffn_bf16_t(const uint16_t* xd, const int32_t* row_token, int64_t x_rows,
                              const int32_t* offsets, const uint16_t* w1, const float* b1,
                              const uint16_t* w2, const float* b2, uint16_t* hbuf, float* y,
                              int E, int h, int F, int64_t A, int64_t cap, int64_t r_max,
@@ -988,7 +998,7 @@ hipError_t launch_ffn_bf16_t(const uint16_t* xd, const int32_t* row_token,
   const int64_t avg = (A + E - 1) / E;
   const int64_t rows_typ = avg < cap ? avg : cap;
   const int64_t rows_max = A < cap ? A : cap;
-  if (row_token && !takes_stream_shape(true, F, rows_typ)) {
+  if (row_token && takes_wide_shape(true, F, rows_typ) && x_rows * h > (int64_t)UINT32_MAX) {
     hipError_t err = launch_gather_rows(xd, row_token, offsets, E, (int64_t)h * 2, r_max, y, s);
     if (err != hipSuccess) return err;
     xd = (const uint16_t*)y;
@@ -1003,15 +1013,16 @@ hipError_t launch_ffn_bf16_t(const uint16_t* xd, const int32_t* row_token,
 
 }  // namespace
 
-hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* row_token, const int32_t* offsets,
-                           const uint16_t* w1, const float* b1, const uint16_t* w2,
-                           const float* b2, uint16_t* hbuf, float* y, int E, int h, int F,
-                           int64_t A, int64_t cap, int64_t r_max, bool packed, hipStream_t s) {
+hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* row_token, int64_t x_rows,
+                           const int32_t* offsets, const uint16_t* w1, const float* b1,
+                           const uint16_t* w2, const float* b2, uint16_t* hbuf, float* y, int E,
+                           int h, int F, int64_t A, int64_t cap, int64_t r_max, bool packed,
+                           hipStream_t s) {
   if (packed)
-    return launch_ffn_bf16_t<true>(xd, row_token, offsets, w1, b1, w2, b2, hbuf, y, E, h, F, A,
-                                   cap, r_max, s);
-  return launch_ffn_bf16_t<false>(xd, row_token, offsets, w1, b1, w2, b2, hbuf, y, E, h, F, A,
-                                  cap, r_max, s);
+    return launch_ffn_bf16_t<true>(xd, row_token, x_rows, offsets, w1, b1, w2, b2, hbuf, y, E,
+                                   h, F, A, cap, r_max, s);
+  return launch_ffn_bf16_t<false>(xd, row_token, x_rows, offsets, w1, b1, w2, b2, hbuf, y, E, h,
+                                  F, A, cap, r_max, s);
 }
 
 hipError_t launch_pack_weights(const uint16_t* w, uint16_t* wp, int E, int N, int Kd,

@@ -198,12 +198,13 @@ hipError_t launch_fp8_dequantize(const uint8_t* xq, const float* scale, const in
                                  int E, int h, int64_t r_max, uint16_t* x_disp, hipStream_t s);
 
 // row_token == nullptr: xd holds the dispatched rows; else xd is the token
-// matrix x and row r reads x[row_token[r]] (y's storage may serve as the
-// staging buffer of that gather).
-hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* row_token, const int32_t* offsets,
-                           const uint16_t* w1, const float* b1, const uint16_t* w2,
-                           const float* b2, uint16_t* hbuf, float* y, int E, int h, int F,
-                           int64_t A, int64_t cap, int64_t r_max, bool packed, hipStream_t s);
+// matrix x (x_rows rows) and row r reads x[row_token[r]] (y's storage may
+// serve as the staging buffer of that gather).
+hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* row_token, int64_t x_rows,
+                           const int32_t* offsets, const uint16_t* w1, const float* b1,
+                           const uint16_t* w2, const float* b2, uint16_t* hbuf, float* y, int E,
+                           int h, int F, int64_t A, int64_t cap, int64_t r_max, bool packed,
+                           hipStream_t s);
 // Row-major [E, N, K] bf16 -> packed fragment blocks (N % 32 == 0, K % 64 == 0).
 hipError_t launch_pack_weights(const uint16_t* w, uint16_t* wp, int E, int N, int Kd,
                                hipStream_t s);

@@ -168,9 +168,11 @@ def test_ffn_ragged_segments(T, h, E, K, F, cf, packed):
     (None, (2048, 768, 14, 1, 3072, 1.0), True),           # ragged, static tile map
     (None, (1000, 256, 4, 1, 320, 1.0), False),            # 250-row experts: tile search
     (None, (513, 64, 64, 6, 128, 1.0), True),              # many small / empty experts
-    (None, (2500, 192, 3, 1, 448, 1.5), True),             # long segments: copy into y first
+    (None, (2500, 192, 3, 1, 448, 1.5), True),             # long segments: tiled kernel
+    (None, (4096, 256, 4, 1, 512, 1.0), False),            # wide kernel, 256 x 256 tiles
+    (None, (3000, 128, 4, 1, 384, 1.3), True),             # wide kernel, 128 x 128 tiles
     (None, (1, 64, 1, 1, 64, 1.0), False),
-    (1, None, False)])                                      # fp32: copy into y first
+    (1, None, False)])                                      # fp32: rows copied into y first
 def test_ffn_rows_equals_ffn_on_x_disp(cid, shape, packed):
     """moe_expert_ffn_rows on x and row_token gives the same H and Y, bit for
     bit, as moe_expert_ffn(_packed) on x_disp[r] = x[row_token[r]]."""

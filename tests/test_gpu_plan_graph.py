@@ -38,7 +38,8 @@ def test_plan_and_graph_replay_match_eager(cid, packed, tail, gather):
     combine and ledger in one moe_combine_ledger call (one launch for
     workloads 1 and 2, two for workload 5's 98304 routes).  gather: the
     dispatch moves no row and moe_expert_ffn_rows gathers them (in the first
-    GEMM's loads for workloads 2 and 4, by a copy into y first for 1 and 5)."""
+    GEMM's loads for the bf16 workloads, by a copy into y first for the fp32
+    workload 1)."""
     banner(f"plan/graph config {cid} packed={packed} tail={tail} gather={gather}")
     inp = device_inputs(cid)
     cfg = inp.cfg
