@@ -246,7 +246,9 @@ int moe_pack_expert_weights(const moe_cfg* cfg, const void* w1, const void* w2,
  * storage that the first GEMM reads before the second writes y.  Pairs with
  * moe_dispatch(x_disp = NULL), which then moves no row.
  *   x [T, h] dtype (16-byte aligned); row_token [R_max] int32 from
- *   moe_dispatch; the other arguments as for moe_expert_ffn. */
+ *   moe_dispatch (its first R entries must lie in [0, T): they are used as
+ *   row indices of x without a check); the other arguments as for
+ *   moe_expert_ffn.  y's storage may serve as staging for the rows. */
 int moe_expert_ffn_rows(const moe_cfg* cfg, int64_t capacity, const void* x,
                         const int32_t* row_token, const int32_t* expert_offsets,
                         const void* w1, const float* b1, const void* w2, const float* b2,
