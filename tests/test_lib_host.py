@@ -120,6 +120,22 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert lib.moe_dispatch_fp8(ctypes.byref(cfg), None, None, None, 2, None, None, None,
                                 None, None, None, None, 0, None) == 1
     assert lib.moe_fp8_dequantize(ctypes.byref(cfg), 2, None, None, None, None, None) == 1
+    # ffn on gathered rows: NULL cfg, NULL row_token, packed fp32 weights
+    assert lib.moe_expert_ffn_rows(None, 2, None, None, None, None, None, None, None, None,
+                                   None, 0, None) == 1
+    assert lib.moe_expert_ffn_rows(ctypes.byref(cfg), 2, None, None, None, None, None, None,
+                                   None, None, None, 0, None) == 1
+    assert lib.moe_expert_ffn_rows(ctypes.byref(cfg32), 2, None, ctypes.c_void_p(16), None,
+                                   None, None, None, None, None, None, 1, None) == 5
+    # combine + ledger: NULL workspace, n_ep out of range, stage too small
+    fake = ctypes.c_void_p(256)
+    assert lib.moe_combine_ledger(ctypes.byref(cfg), None, None, None, None, None, None, fake,
+                                  2, fake, 1 << 20, None, 0, None) == 1
+    ws_b = lib.moe_workspace_bytes(ctypes.byref(cfg))
+    assert lib.moe_combine_ledger(ctypes.byref(cfg), None, fake, fake, fake, fake, fake, fake,
+                                  65, fake, 1 << 20, fake, ws_b, None) == 1
+    assert lib.moe_combine_ledger(ctypes.byref(cfg), None, fake, fake, fake, fake, fake, fake,
+                                  2, fake, 8, fake, ws_b, None) == 3
 
 
 def test_empty_batch_needs_no_device_work(lib):
