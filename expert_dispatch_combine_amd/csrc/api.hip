@@ -282,7 +282,7 @@ int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* route_row,
 
 size_t moe_ledger_stage_bytes(const moe_cfg* cfg, int32_t n_ep) {
   if (check_cfg(cfg) != MOE_OK || n_ep < 1 || n_ep > kMaxRanks) return 0;
-  return ledger_final_bytes(cfg->E, n_ep);
+  return ledger_stage_bytes(cfg->E, n_ep);
 }
 
 // Checks shared by moe_ledger_launch and moe_ledger.
@@ -307,7 +307,7 @@ int moe_ledger_launch(const moe_cfg* cfg, const int32_t* topk_idx, const float* 
                        ws_bytes);
   if (st != MOE_OK) return st;
   if (!host_stage) return MOE_ERR_INVALID_ARG;
-  if (stage_bytes < ledger_final_bytes(cfg->E, n_ep)) return MOE_ERR_SHAPE;
+  if (stage_bytes < ledger_stage_bytes(cfg->E, n_ep)) return MOE_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   // page-locked host memory mapped into the device: the kernels write the
   // stage themselves; otherwise the final area is copied into it
@@ -336,7 +336,7 @@ int moe_combine_ledger(const moe_cfg* cfg, const float* y, const int32_t* route_
   if (st != MOE_OK) return st;
   if (cfg->T > 0 && !out) return MOE_ERR_INVALID_ARG;
   if (!host_stage) return MOE_ERR_INVALID_ARG;
-  if (stage_bytes < ledger_final_bytes(cfg->E, n_ep)) return MOE_ERR_SHAPE;
+  if (stage_bytes < ledger_stage_bytes(cfg->E, n_ep)) return MOE_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   void* mapped = nullptr;  // as in moe_ledger_launch
   if (hipHostGetDevicePointer(&mapped, host_stage, 0) != hipSuccess) {
@@ -363,11 +363,20 @@ int moe_ledger_finalize(const moe_cfg* cfg, int64_t capacity, int32_t n_ep, doub
   if (!out || !host_stage || capacity < 0) return MOE_ERR_INVALID_ARG;
   if (n_ep < 1 || n_ep > kMaxRanks) return MOE_ERR_INVALID_ARG;
   const int T = cfg->T, K = cfg->K, E = cfg->E;
+  // add the stage's integer partials (two's complement: any order is exact)
   const char* stage = (const char*)host_stage;
-  const int64_t* h_load = (const int64_t*)stage;
-  const uint64_t* h_P = (const uint64_t*)(stage + (size_t)E * 8);  // units of 2^-32
-  const int64_t* h_cnt = (const int64_t*)(stage + (size_t)2 * E * 8);
-  const int64_t* h_pair = (const int64_t*)(stage + (size_t)(2 * E + LC_N) * 8);
+  const int64_t parts = *(const int64_t*)stage;
+  if (parts < 1 || parts > kLedgerStageParts) return MOE_ERR_INVALID_ARG;
+  const size_t nw = ledger_final_bytes(E, n_ep) / 8;
+  std::vector<uint64_t> sum(nw, 0);
+  for (int64_t q = 0; q < parts; ++q) {
+    const uint64_t* part = (const uint64_t*)(stage + 8 + (size_t)q * nw * 8);
+    for (size_t w = 0; w < nw; ++w) sum[w] += part[w];
+  }
+  const int64_t* h_load = (const int64_t*)sum.data();
+  const uint64_t* h_P = sum.data() + E;  // units of 2^-32
+  const int64_t* h_cnt = (const int64_t*)(sum.data() + 2 * E);
+  const int64_t* h_pair = (const int64_t*)(sum.data() + 2 * E + LC_N);
 
   const int64_t A = routes_of(cfg);
   const int64_t be = elem_bytes(cfg);

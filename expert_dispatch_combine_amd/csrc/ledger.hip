@@ -54,14 +54,15 @@ LedgerWs carve(void* ws, int64_t A, int E, int n_ep) {
   w.blk_pair = (int32_t*)(p + o);
   o = align_up(o + (size_t)nb * n_ep * n_ep * sizeof(int32_t), 256);
   w.fin = p + o;
-  w.fin_bytes = ledger_final_bytes(E, n_ep);
+  w.fin_bytes = ledger_stage_bytes(E, n_ep);
   o = align_up(o + w.fin_bytes, 256);
   w.total = o;
   return w;
 }
 
 // Final area layout (8 bytes each): loads[E] int64, P[E] uint64 (units of
-// 2^-32), counters[LC_N] int64, pair[n_ep * n_ep] int64.
+// 2^-32), counters[LC_N] int64, pair[n_ep * n_ep] int64.  The stage holds the
+// part count (int64), then that many final areas of partials.
 struct FinalArea {
   int64_t* load;
   uint64_t* P;
@@ -82,9 +83,9 @@ __device__ __forceinline__ unsigned long long gate_fixed(float g) {
 // LDS of one ledger workgroup, carved from a byte array (8-byte sums first).
 constexpr int kLedgerLdsBytes = kMaxExperts * (8 + 4 + 4) + kMaxRanks * kMaxRanks * 4 + LC_N * 4;
 
-// Workgroup b of the ledger: RPB routes from b * RPB.  FINAL (one workgroup
-// takes every route): write the final area `fin` directly instead of the
-// per-block partials.  `lds`: kLedgerLdsBytes, 8-byte aligned.
+// Workgroup b of the ledger: RPB routes from b * RPB.  FINAL: write part b of
+// the stage `fin` (of nparts parts; workgroup 0 writes the count) instead of
+// the per-block partials.  `lds`: kLedgerLdsBytes, 8-byte aligned.
 template <int RPB, bool FINAL>
 __device__ __forceinline__ void ledger_block(
     int b, const int32_t* __restrict__ idx, const float* __restrict__ gate,
@@ -92,7 +93,7 @@ __device__ __forceinline__ void ledger_block(
     const int32_t* __restrict__ owner, int64_t A, int K, int E, int n_ep,
     int32_t* __restrict__ blk_load, uint64_t* __restrict__ blk_P,
     int64_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_pair, char* __restrict__ fin,
-    char* lds) {
+    int nparts, char* lds) {
   constexpr int PER_THREAD = RPB / 256;
   unsigned long long* s_P = (unsigned long long*)lds;
   int* s_load = (int*)(lds + kMaxExperts * 8);
@@ -176,7 +177,8 @@ __device__ __forceinline__ void ledger_block(
   __syncthreads();
 
   if (FINAL) {
-    const FinalArea f = final_area(fin, E);
+    if (b == 0 && tid == 0) *(int64_t*)fin = nparts;
+    const FinalArea f = final_area(fin + 8 + (size_t)b * ledger_final_bytes(E, n_ep), E);
     for (int e = tid; e < E; e += 256) {
       f.P[e] = s_P[e];
       f.load[e] = s_load[e];
@@ -202,27 +204,29 @@ __global__ __launch_bounds__(256) void ledger_partial_kernel(
     int64_t* __restrict__ blk_cnt, int32_t* __restrict__ blk_pair, char* __restrict__ fin) {
   __shared__ __attribute__((aligned(16))) char lds[kLedgerLdsBytes];
   ledger_block<RPB, FINAL>(blockIdx.x, idx, gate, route_row, src, owner, A, K, E, n_ep,
-                           blk_load, blk_P, blk_cnt, blk_pair, fin, lds);
+                           blk_load, blk_P, blk_cnt, blk_pair, fin, 1, lds);
 }
 
-// The combine and the one-workgroup ledger in one launch: block 0 (dispatched
-// first, and the longest) is the ledger, blocks 1.. the combine's workgroups.
-// The two read the same routes and write disjoint outputs.
+// The combine and the ledger in one launch: blocks 0 .. nled-1 (dispatched
+// first, and the longest) each count kLedgerPartRoutes routes into their own
+// part of the stage, blocks nled.. are the combine's workgroups.  The two
+// read the same routes and write disjoint outputs.
+constexpr int kLedgerPartRoutes = kSmallLedgerRoutes / kLedgerStageParts;
 template <bool VEC, int U>
 __global__ __launch_bounds__(256) void combine_ledger_kernel(
     const float* __restrict__ y, const int32_t* __restrict__ route_row,
     const float* __restrict__ gate, float* __restrict__ out, int T, int K, int h, int TB,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ src,
-    const int32_t* __restrict__ owner, int E, int n_ep, char* __restrict__ fin) {
+    const int32_t* __restrict__ owner, int E, int n_ep, int nled, char* __restrict__ fin) {
   constexpr int LDS = kLedgerLdsBytes > kCombineLdsBytes ? kLedgerLdsBytes : kCombineLdsBytes;
   __shared__ __attribute__((aligned(16))) char lds[LDS];
-  if (blockIdx.x == 0) {
-    ledger_block<kSmallLedgerRoutes, true>(0, idx, gate, route_row, src, owner, (int64_t)T * K,
-                                           K, E, n_ep, nullptr, nullptr, nullptr, nullptr, fin,
-                                           lds);
+  if ((int)blockIdx.x < nled) {
+    ledger_block<kLedgerPartRoutes, true>(blockIdx.x, idx, gate, route_row, src, owner,
+                                          (int64_t)T * K, K, E, n_ep, nullptr, nullptr, nullptr,
+                                          nullptr, fin, nled, lds);
     return;
   }
-  combine_tokens<VEC, U>(blockIdx.x - 1, y, route_row, gate, out, T, K, h, TB, (int*)lds,
+  combine_tokens<VEC, U>(blockIdx.x - nled, y, route_row, gate, out, T, K, h, TB, (int*)lds,
                          (float*)(lds + kMaxTB * kMaxTopK * 4));
 }
 
@@ -236,8 +240,9 @@ __global__ __launch_bounds__(256) void ledger_reduce_kernel(
   const int lane = threadIdx.x & 63;
   const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int items = 2 * E + LC_N + np;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *(int64_t*)fin = 1;  // one part
   if (q >= items) return;  // whole waves leave together
-  const FinalArea fa = final_area(fin, E);
+  const FinalArea fa = final_area(fin + 8, E);
   uint64_t s = 0;  // two's complement: signed partials add up the same way
   if (q < E) {
     for (int b = lane; b < nb; b += 64) s += (uint64_t)(int64_t)blk_load[(size_t)b * E + q];
@@ -312,10 +317,11 @@ hipError_t launch_combine_ledger(const float* y, const int32_t* route_row, const
   *final_area_out = fin;
   *final_bytes = w.fin_bytes;
   const CombineShape c = combine_shape(T, h);
+  const int nled = (int)((A + kLedgerPartRoutes - 1) / kLedgerPartRoutes);
   with_combine_variant(c, [&](auto vec, auto u) {
     hipLaunchKernelGGL((combine_ledger_kernel<decltype(vec)::value, decltype(u)::value>),
-                       dim3(c.grid + 1), dim3(256), 0, s, y, route_row, gate, out, T, K, h,
-                       c.TB, idx, src, owner, E, n_ep, fin);
+                       dim3(c.grid + nled), dim3(256), 0, s, y, route_row, gate, out, T, K, h,
+                       c.TB, idx, src, owner, E, n_ep, nled, fin);
   });
   return hipGetLastError();
 }

@@ -60,8 +60,15 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 size_t dispatch_ws_bytes(int64_t A, int E);
 size_t ledger_ws_bytes(int64_t A, int E, int n_ep);
 // Bytes of the ledger's compact result (device final area == host stage).
-inline size_t ledger_final_bytes(int E, int n_ep) {
+__host__ __device__ inline size_t ledger_final_bytes(int E, int n_ep) {
   return (size_t)(2 * E + LC_N + n_ep * n_ep) * 8;
+}
+// The ledger's stage: an int64 count of parts, then up to kLedgerStageParts
+// final areas of integer partials, which the host adds (exactly, in any
+// order) when it decodes the stage.
+constexpr int kLedgerStageParts = 4;
+inline size_t ledger_stage_bytes(int E, int n_ep) {
+  return 8 + (size_t)kLedgerStageParts * ledger_final_bytes(E, n_ep);
 }
 
 // ---------------------------------------------------------------- launchers

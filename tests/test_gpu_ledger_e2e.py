@@ -143,9 +143,10 @@ def test_ledger_empty_and_errors():
     (37, 30, 3, 3, 2, 0.5, "f32", False),         # scalar rows, K = E, heavy drops
     (1, 64, 1, 1, 1, 1.0, "bf16", True)])
 def test_combine_ledger_equals_the_two_calls(T, h, E, K, n_ep, cf, dtype, pinned):
-    """moe_combine_ledger gives the same `out` (bit for bit) and the same stage
-    bytes as moe_combine followed by moe_ledger_launch, and its ledger equals
-    the oracle's."""
+    """moe_combine_ledger gives the same `out` (bit for bit) and the same
+    decoded ledger as moe_combine followed by moe_ledger_launch (its stage may
+    hold the counters in several integer parts), and that ledger equals the
+    oracle's."""
     banner(f"combine+ledger T={T} h={h} E={E} K={K} pinned={pinned}")
     rng = np.random.default_rng(T * 31 + h)
     idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
@@ -174,8 +175,8 @@ def test_combine_ledger_equals_the_two_calls(T, h, E, K, n_ep, cf, dtype, pinned
                          n_ep, st_one, ws)
     torch.cuda.synchronize()
     assert torch.equal(out_one, out_two)
-    assert torch.equal(st_one, st_two)
     g = M.moe_ledger_finalize(mc, cap, n_ep, 0.01, st_one)
+    assert g == M.moe_ledger_finalize(mc, cap, n_ep, 0.01, st_two)
     o = O.ledger(idx, gate, sl["route_row"], cap, src, owner, n_ep, h, 2 if dtype == "bf16" else 4)
     _compare_ledger(g, o)
 
