@@ -18,10 +18,11 @@
 // Device part: one workgroup per 512 routes builds LDS histograms and a
 // second kernel adds the per-block partials (one wave per output value).  Up
 // to kSmallLedgerRoutes routes one workgroup takes them all and writes the
-// final area itself; that workgroup can also run as block 0 of the combine's
-// launch (combine_ledger_kernel), beside the combine's own workgroups.  The
-// final area may be page-locked host memory (its device address), which
-// spares a copy.  The host finishes the few scalar formulas in float64.
+// final area itself.  In the combine's launch (combine_ledger_kernel) the
+// first workgroups count 1024 routes each into parts of the stage of their
+// own, which the host adds.  The stage may be page-locked host memory (its
+// device address), which spares a copy.  The host finishes the few scalar
+// formulas in float64.
 #include "combine_block.hpp"
 
 namespace moe {

@@ -307,8 +307,9 @@ int moe_ledger_finalize(const moe_cfg* cfg, int64_t capacity, int32_t n_ep, doub
  * the arguments of both, the same `out` and the same `host_stage` contents
  * (decode them with moe_ledger_finalize once the stream has passed the
  * call).  Up to 4096 routes (T*K) both run in ONE launch, the ledger's
- * single workgroup beside the combine's, which spares the second launch's
- * fixed cost; above that it enqueues the two calls' kernels in turn.  The
+ * workgroups (one per 1024 routes, each writing its own integer partials
+ * into the stage, which moe_ledger_finalize adds) beside the combine's;
+ * above that it enqueues the two calls' kernels in turn.  The
  * workspace is the ledger's (moe_workspace_bytes) and must not be reused
  * before the stage copy is done, as for moe_ledger_launch. */
 int moe_combine_ledger(const moe_cfg* cfg, const float* y, const int32_t* route_row,
