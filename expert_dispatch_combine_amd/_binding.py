@@ -347,6 +347,7 @@ def moe_ledger(cfg: MoeCfg, topk_idx, topk_gate, route_row, capacity: int, src_r
     wsp, wsb = _ws(ws)
     E = int(cfg.E)
     out = MoeLedger()
+    out.status = -1  # moe_ledger fills `out` (status included) only once it has counted
     loads = (_I64 * E)()
     f = (_F64 * E)()
     P = (_F64 * E)()
@@ -357,7 +358,7 @@ def moe_ledger(cfg: MoeCfg, topk_idx, topk_gate, route_row, capacity: int, src_r
                         _ptr(src_rank, "i32", cfg, "src_rank"),
                         _ptr(owner_rank, "i32", cfg, "owner_rank"), int(n_ep), float(alpha),
                         ctypes.byref(out), loads, f, P, pair, wsp, wsb, _stream(stream))
-    if st != 0 and (raise_on_error or st not in (2, 1)):
+    if st != 0 and (raise_on_error or st not in (2, 1) or out.status != st):
         raise MoeError("moe_ledger", st)
     d = out.as_dict()
     d["loads"] = list(loads)
@@ -424,9 +425,10 @@ def moe_ledger_finalize(cfg: MoeCfg, capacity: int, n_ep: int, alpha: float,
     f = (_F64 * E)()
     P = (_F64 * E)()
     pair = (_I64 * (n_ep * n_ep))()
+    out.status = -1  # finalize fills `out` (status included) only for a decoded stage
     st = lib.moe_ledger_finalize(ctypes.byref(cfg), int(capacity), int(n_ep), float(alpha), hp,
                                  ctypes.byref(out), loads, f, P, pair)
-    if st != 0 and (raise_on_error or st not in (2, 1)):
+    if st != 0 and (raise_on_error or st not in (2, 1) or out.status != st):
         raise MoeError("moe_ledger_finalize", st)
     d = out.as_dict()
     d["loads"] = list(loads)

@@ -2,6 +2,8 @@
 // launches on the caller's stream, and the ledger's host-side float64 math.
 // Declarations and contracts are in include/moe.h.
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -366,7 +368,8 @@ int moe_ledger_finalize(const moe_cfg* cfg, int64_t capacity, int32_t n_ep, doub
   // add the stage's integer partials (two's complement: any order is exact)
   const char* stage = (const char*)host_stage;
   const int64_t parts = *(const int64_t*)stage;
-  if (parts < 1 || parts > kLedgerStageParts) return MOE_ERR_INVALID_ARG;
+  // a stage that no ledger launch has completed (zeroed, torn, stale layout)
+  if (parts < 1 || parts > kLedgerStageParts) return MOE_ERR_SHAPE;
   const size_t nw = ledger_final_bytes(E, n_ep) / 8;
   std::vector<uint64_t> sum(nw, 0);
   for (int64_t q = 0; q < parts; ++q) {
@@ -463,9 +466,15 @@ int moe_recommend_plan(const moe_ledger_t* L, const double* thresholds, int32_t 
   const int64_t loc_total = L->local_routes + L->cross_rank_routes;
   const double cross =
       (use_locality && loc_total > 0) ? (double)L->cross_rank_routes / (double)loc_total : 0.0;
-  if (L->overflow == 0 && L->balance_ratio <= th[0] && cross <= th[1]) return MOE_PLAN_ACCEPT;
-  if (overflow_share <= th[2] && L->balance_ratio <= th[3] && cross <= th[4])
-    return MOE_PLAN_TUNE;
+  // The decision reads the balance ratio as the summary stores it, rounded
+  // to 3 decimals ([EP46] Step 4 reference summary).  "%.3f" rounds the exact
+  // binary value to the nearest 3-decimal string (ties to even) and strtod
+  // returns the double nearest to that string, as Python's round(x, 3) does.
+  char txt[64];
+  std::snprintf(txt, sizeof(txt), "%.3f", L->balance_ratio);
+  const double bal = std::strtod(txt, nullptr);
+  if (L->overflow == 0 && bal <= th[0] && cross <= th[1]) return MOE_PLAN_ACCEPT;
+  if (overflow_share <= th[2] && bal <= th[3] && cross <= th[4]) return MOE_PLAN_TUNE;
   return MOE_PLAN_REJECT;
 }
 

@@ -224,8 +224,9 @@ hipError_t launch_combine(const float* y, const int32_t* route_row, const float*
                           float* out, int T, int K, int h, hipStream_t s);
 
 // Ledger: per-block partials then a fixed-order reduction into `final_area`
-// (layout: loads[E] int64 | P[E] double | counters[LC_N] int64 |
-//  pairs[n_ep*n_ep] int64).
+// (layout: loads[E] int64 | P[E] uint64, sums of gates in units of 2^-32 |
+//  counters[LC_N] int64 | pairs[n_ep*n_ep] int64), preceded by the stage's
+// int64 part count.
 // fin_dst: device-accessible destination of the final area (e.g. the device
 // address of page-locked host memory), or NULL for the area in `ws`.
 hipError_t launch_ledger(const int32_t* idx, const float* gate, const int32_t* route_row,
@@ -233,8 +234,10 @@ hipError_t launch_ledger(const int32_t* idx, const float* gate, const int32_t* r
                          int n_ep, void* ws, void* fin_dst, void** final_area,
                          size_t* final_bytes, hipStream_t s);
 // The combine and the ledger of the same routes: one launch up to
-// kSmallLedgerRoutes routes (the ledger's one workgroup beside the combine's),
-// else launch_combine then launch_ledger.  Same results as those two.
+// kSmallLedgerRoutes routes (one ledger workgroup per 1024 routes, each
+// writing its own integer partials into the stage, beside the combine's
+// workgroups), else launch_combine then launch_ledger.  Same out and the same
+// decoded ledger as those two.
 hipError_t launch_combine_ledger(const float* y, const int32_t* route_row, const float* gate,
                                  float* out, const int32_t* idx, const int32_t* src,
                                  const int32_t* owner, int T, int K, int h, int E, int n_ep,

@@ -224,10 +224,13 @@ class LayerPlan:
     def decode(self) -> int:
         """moe_ledger_finalize of the completed stage into the plan's own host
         buffers (no Python objects built); returns its status (0, or 1/2
-        when the batch held invalid ranks / expert ids)."""
+        when the batch held invalid ranks / expert ids, with the ledger
+        filled).  A stage holding no completed ledger, or an argument error,
+        raises."""
         fn, args = self.finalize
+        self._fin[0].status = -1  # written by finalize only for a decoded stage
         st = fn(*args)
-        if st not in (0, 1, 2):
+        if st != 0 and (st not in (1, 2) or self._fin[0].status != st):
             raise MoeError("moe_ledger_finalize", st)
         return st
 

@@ -298,15 +298,24 @@ int moe_ledger_launch(const moe_cfg* cfg, const int32_t* topk_idx, const float* 
                       const int32_t* route_row, const int32_t* src_rank,
                       const int32_t* owner_rank, int32_t n_ep, void* host_stage,
                       size_t stage_bytes, void* ws, size_t ws_bytes, void* stream);
+/* moe_ledger_finalize returns MOE_ERR_SHAPE, and leaves every output
+ * unwritten, for a stage that holds no completed ledger (its part count is
+ * outside 1..4: zeroed, torn or never written).  Otherwise its statuses are
+ * moe_ledger's, with `out` filled: MOE_OK, MOE_ERR_EXPERT_ID for ids outside
+ * [0, E), MOE_ERR_INVALID_ARG for source or owner ranks outside [0, n_ep)
+ * (out->status then holds the same code); argument errors (NULL pointers,
+ * capacity < 0, n_ep outside 1..64) return MOE_ERR_INVALID_ARG with `out`
+ * unwritten, so a caller tells the two apart by out->status. */
 int moe_ledger_finalize(const moe_cfg* cfg, int64_t capacity, int32_t n_ep, double alpha,
                         const void* host_stage, moe_ledger_t* out, int64_t* loads,
                         double* f, double* P, int64_t* pair_routes);
 
 /* moe_combine and moe_ledger_launch of the same routes in one call ([EP46]
  * combine_expert_outputs and summarize; [EPC] Combine; [EP47] summarize):
- * the arguments of both, the same `out` and the same `host_stage` contents
- * (decode them with moe_ledger_finalize once the stream has passed the
- * call).  Up to 4096 routes (T*K) both run in ONE launch, the ledger's
+ * the arguments of both, the same `out`, and a `host_stage` that
+ * moe_ledger_finalize decodes to the same ledger once the stream has passed
+ * the call (its part count and byte layout may differ from
+ * moe_ledger_launch's).  Up to 4096 routes (T*K) both run in ONE launch, the ledger's
  * workgroups (one per 1024 routes, each writing its own integer partials
  * into the stage, which moe_ledger_finalize adds) beside the combine's;
  * above that it enqueues the two calls' kernels in turn.  The
@@ -325,6 +334,8 @@ int moe_combine_ledger(const moe_cfg* cfg, const float* y, const int32_t* route_
  *   MOE_PLAN_TUNE    overflow / total_routes <= 0.25, balance_ratio <= 1.8 and
  *                    cross-rank share <= 0.9;
  *   MOE_PLAN_REJECT  otherwise, and for an empty batch.
+ * balance_ratio enters the comparisons rounded to 3 decimals (ties to even,
+ * as Python's round(x, 3)), the value that page's summary stores.
  * The cross-rank share is cross_rank_routes / (local_routes +
  * cross_rank_routes) (all routes) when use_locality != 0, else 0.
  * thresholds: NULL, or 5 doubles in the order above (accept balance, accept

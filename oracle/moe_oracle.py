@@ -682,7 +682,12 @@ def recommend_plan(summary: dict, locality: Optional[dict] = None, **thresholds)
     the accept limits; 'tune' when the overflow share, the balance ratio and
     the cross-rank share all stay within the (looser) tune limits; 'reject'
     otherwise, and for an empty batch.  Without a locality summary the
-    cross-rank share counts as 0.  Limits default to the page's values."""
+    cross-rank share counts as 0.  Limits default to the page's values.
+
+    The page's summary stores the balance ratio rounded to 3 decimals (its
+    Step 4 reference summary), and the decision compares that stored value;
+    `summarize_routes` returns it unrounded, so it is rounded here, with
+    Python's round (ties to even on the exact binary value)."""
     th = dict(PLAN_THRESHOLDS, **thresholds)
     A = summary["total_routes"]
     if A == 0:
@@ -691,7 +696,7 @@ def recommend_plan(summary: dict, locality: Optional[dict] = None, **thresholds)
     cross = 0.0
     if locality is not None and locality["total_routes"]:
         cross = locality["cross_rank_routes"] / locality["total_routes"]
-    bal = summary["balance_ratio"]
+    bal = round(summary["balance_ratio"], 3)
     if (summary["overflow"] == 0 and bal <= th["max_accept_balance"]
             and cross <= th["max_accept_cross_rank"]):
         return "accept"

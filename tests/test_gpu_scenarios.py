@@ -69,3 +69,39 @@ def test_routing_scenario(name):
         assert 0.35 < led["local_hit_ratio"] < 0.65 and plan == "accept"
     else:
         assert led["overflow"] > 0 and led["balance_ratio"] > 1.5 and plan == "reject"
+
+
+@pytest.mark.parametrize("loads,cf,want", [([6002, 3998], 1.25, "accept"),
+                                           ([9002, 998], 1.8, "tune"),
+                                           ([12006, 7994], 1.25, "tune")])
+def test_plan_decision_at_the_3_decimal_boundary(loads, cf, want):
+    """[EP46] Step 4 / TODO 3: routings whose balance ratio lies just past a
+    limit but is stored as round(ratio, 3) on it.  Top-1 routes in a seeded
+    order through moe_dispatch, the GPU ledger and moe_recommend_plan decide
+    as the oracle (and the page) does."""
+    banner(f"plan decision loads={loads} cf={cf}")
+    E = len(loads)
+    T = sum(loads)
+    rng = np.random.default_rng(41)
+    ids = rng.permutation(np.repeat(np.arange(E, dtype=np.int32), loads)).reshape(T, 1)
+    cfg = W.custom(T, 64, E, 1, 64, cf=cf, n_ep=2)
+    mc = cfg_from(cfg)
+    b = LayerBuffers(mc, capacity_of(mc))
+    b.topk_idx.copy_(torch.from_numpy(ids))
+    b.topk_gate.fill_(1.0)
+    M.moe_dispatch(mc, None, b.topk_idx, b.capacity, b.expert_offsets, b.route_rank,
+                   b.route_row, b.row_token, None, None, b.ws)
+    src = torch.from_numpy((np.arange(T) % 2).astype(np.int32)).cuda()
+    owner = torch.from_numpy((np.arange(E) % 2).astype(np.int32)).cuda()
+    led = run_ledger(b, src, owner, 2)
+    torch.cuda.synchronize()
+    cap = O.capacity(T, E, cf)
+    sl = O.slot_routes(ids, E, cap)
+    assert np.array_equal(b.route_row.cpu().numpy(), sl["route_row"])
+    oled = O.ledger(ids, np.ones((T, 1)), sl["route_row"], cap, np.arange(T) % 2,
+                    np.arange(E) % 2, 2, hidden_size=64, bytes_per_elem=2)
+    for k in ("total_routes", "overflow", "accepted_routes", "local_routes",
+              "cross_rank_routes", "max_load"):
+        assert led[k] == oled[k], k
+    assert led["balance_ratio"] == oled["balance_ratio"]
+    assert M.moe_recommend_plan(led) == O.recommend_plan(oled, oled) == want

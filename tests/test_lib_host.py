@@ -175,7 +175,11 @@ def test_recommend_plan_matches_the_oracle(lib):
     for _ in range(3000):
         A = rng.choice([0, 1, 7, 100, 1000])
         ovf = rng.randint(0, A)
-        bal = rng.choice([1.0, 1.2, 1.2000001, 1.5, 1.8, 1.8000001, 2.5])
+        bal = rng.choice([1.0, 1.2, 1.2000001, 1.2004, 1.2005, 1.2006, 1.5, 1.8, 1.8000001,
+                          1.8004, 1.8005, 1.8006, 2.5,
+                          # the exact ratio of integer loads, max * E / A
+                          rng.randint(1, 20000) * 2 / 20000, rng.randint(6000, 6010) / 5000,
+                          rng.randint(9000, 9010) / 5000])
         cross = rng.randint(0, A)
         led = {name: 0 for name, _ in M.MoeLedger._fields_}
         led.update(total_routes=A, overflow=ovf, balance_ratio=bal, local_routes=A - cross,
@@ -193,3 +197,34 @@ def test_recommend_plan_matches_the_oracle(lib):
         {"total_routes": 10, "local_routes": 9, "cross_rank_routes": 1},
         max_accept_balance=1.0, max_accept_cross_rank=0.1, max_tune_overflow_ratio=0.5,
         max_tune_balance=3.0, max_tune_cross_rank=1.0)
+
+
+def test_finalize_rejects_a_stage_without_a_ledger(lib):
+    """A zeroed (never written, or torn) stage holds no part count: finalize
+    returns MOE_ERR_SHAPE and leaves every output unwritten."""
+    cfg = M.MoeCfg.make(16, 64, 4, 2, 64, "bf16", 1.0)
+    n_ep = 2
+    nbytes = lib.moe_ledger_stage_bytes(ctypes.byref(cfg), n_ep)
+    assert nbytes > 8
+    stage = (ctypes.c_uint8 * nbytes)()
+    out = M.MoeLedger()
+    out.status = -7
+    out.total_routes = -7
+    loads = (ctypes.c_int64 * 4)(-1, -1, -1, -1)
+    st = lib.moe_ledger_finalize(ctypes.byref(cfg), 8, n_ep, 0.01, stage, ctypes.byref(out),
+                                 loads, None, None, None)
+    assert st == 3  # MOE_ERR_SHAPE
+    assert out.status == -7 and out.total_routes == -7 and list(loads) == [-1] * 4
+    # a part count beyond the stage's capacity is refused the same way
+    ctypes.c_int64.from_buffer(stage).value = 5
+    assert lib.moe_ledger_finalize(ctypes.byref(cfg), 8, n_ep, 0.01, stage, ctypes.byref(out),
+                                   loads, None, None, None) == 3
+    # one part of all-zero counters is a valid (empty) ledger
+    ctypes.c_int64.from_buffer(stage).value = 1
+    assert lib.moe_ledger_finalize(ctypes.byref(cfg), 8, n_ep, 0.01, stage, ctypes.byref(out),
+                                   loads, None, None, None) == 0
+    assert out.status == 0 and out.total_routes == 32 and list(loads) == [0] * 4
+    # the Python decoder raises on a zeroed stage instead of returning zeros
+    import torch
+    with pytest.raises(M.MoeError):
+        M.moe_ledger_finalize(cfg, 8, n_ep, 0.01, torch.zeros(nbytes, dtype=torch.uint8))

@@ -508,11 +508,100 @@ def test_plan_decision_boundaries():
 
     assert O.recommend_plan(summ(0, 0, 0.0)) == "reject"
     assert O.recommend_plan(summ(100, 0, 1.2), loc(50)) == "accept"
-    assert O.recommend_plan(summ(100, 0, 1.2 + 1e-12), loc(50)) == "tune"
+    # the balance ratio is compared as the summary stores it, round(., 3)
+    assert O.recommend_plan(summ(100, 0, 1.2004), loc(50)) == "accept"
+    assert O.recommend_plan(summ(100, 0, 1.2006), loc(50)) == "tune"
     assert O.recommend_plan(summ(100, 0, 1.0), loc(51)) == "tune"
     assert O.recommend_plan(summ(100, 1, 1.0), loc(0)) == "tune"
     assert O.recommend_plan(summ(100, 25, 1.8), loc(90)) == "tune"
     assert O.recommend_plan(summ(100, 26, 1.0), loc(0)) == "reject"
-    assert O.recommend_plan(summ(100, 0, 1.8 + 1e-12), loc(0)) == "reject"
+    assert O.recommend_plan(summ(100, 0, 1.8004), loc(0)) == "tune"
+    assert O.recommend_plan(summ(100, 0, 1.8006), loc(0)) == "reject"
     assert O.recommend_plan(summ(100, 0, 1.0), loc(91)) == "reject"
     assert O.recommend_plan(summ(100, 0, 1.0), loc(0, total=0)) == "accept"
+
+
+def test_plan_decision_reads_the_stored_3_decimal_balance():
+    """[EP46] Step 4 reference code: the summary stores round(balance_ratio, 3)
+    and the joint decision (TODO 3) compares that stored value with its
+    limits.  Routings whose exact ratio lies just past a limit but rounds onto
+    it decide as on the page.  The page's decision is evaluated here by its
+    own rule on the rounded value."""
+    def page(loads, E, cf):
+        routes = [[e] for e in range(E) for _ in range(loads[e])]
+        return O.summarize_routes(routes, E, 8, 2, cf)
+
+    # 6002 / 3998 routes over 2 experts, cf 1.25: cap 6250, no overflow,
+    # balance 1.2004 -> stored 1.2 -> accept (the unrounded value would tune)
+    s = page([6002, 3998], 2, 1.25)
+    assert s["overflow"] == 0 and s["balance_ratio"] > 1.2
+    assert O.recommend_plan(s) == "accept"
+    # 9002 / 998 routes, cf 1.8: cap 9000, overflow 2 (share 2e-4), balance
+    # 1.8004 -> stored 1.8 -> tune (the unrounded value would reject)
+    s = page([9002, 998], 2, 1.8)
+    assert s["overflow"] == 2 and s["balance_ratio"] > 1.8
+    assert O.recommend_plan(s) == "tune"
+    # 12005 / 7995: the double nearest 1.2005 lies below the decimal
+    # midpoint, so it rounds to 1.2 and accepts; 12006 / 7994 rounds to 1.201
+    s = page([12005, 7995], 2, 1.25)
+    assert round(s["balance_ratio"], 3) == 1.2 and O.recommend_plan(s) == "accept"
+    s = page([12006, 7994], 2, 1.25)
+    assert round(s["balance_ratio"], 3) == 1.201 and O.recommend_plan(s) == "tune"
+
+
+def test_expert_loads_match_the_pages_worked_examples():
+    """[EP47] 测试: the route ledgers of the worked examples assert the loads
+    [2, 2, 2], [3, 1], [10, 1] and [0, 0] (empty)."""
+    g = _load("ep47_ledger_cases.json")
+    for case in g["cases"]:
+        E = case["num_experts"]
+        routes = case["routes"]
+        want = case["expect"]["expert_loads"]
+        if routes:
+            K = len(routes[0])
+            if all(len(r) == K for r in routes):
+                idx = np.asarray(routes, np.int64).reshape(len(routes), K)
+                assert O.expert_loads(idx, E).tolist() == want, case["name"]
+        flat = np.asarray([e for r in routes for e in r], np.int64).reshape(-1, 1)
+        assert O.expert_loads(flat, E).tolist() == want, case["name"]
+
+
+def test_expert_loads_against_an_independent_count():
+    """Every routing with T <= 4 tokens, E <= 3 experts and K <= 2 distinct
+    experts per token, plus random large ones: the loads equal numpy's
+    bincount of the ids (a library count, independent of the oracle's loop)."""
+    import itertools
+    for E in (1, 2, 3):
+        for K in range(1, min(E, 2) + 1):
+            choices = list(itertools.permutations(range(E), K))
+            for T in range(0, 5 if E < 3 else 4):
+                for combo in itertools.product(choices, repeat=T):
+                    idx = np.asarray(combo, np.int64).reshape(T, K)
+                    want = np.bincount(idx.reshape(-1), minlength=E)
+                    assert np.array_equal(O.expert_loads(idx, E), want)
+    rng = np.random.default_rng(31)
+    for T, E, K in [(1000, 16, 1), (513, 64, 6), (77, 256, 8)]:
+        idx = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+        want = np.bincount(idx.reshape(-1), minlength=E)
+        assert np.array_equal(O.expert_loads(idx, E), want)
+
+
+def test_bias_update_bit_exact_against_the_pages_torch_expression():
+    """[DSV3] section 八 DeepSeekV3Gate: with fp32 tensors, expert_count =
+    bincount(...).float(); mean_count = expert_count.mean(); expert_bias.data
+    += alpha * (mean_count - expert_count).  The page's expression, run by
+    torch on the CPU, equals the oracle's update bit for bit."""
+    rng = np.random.default_rng(32)
+    for trial in range(300):
+        E = int(rng.choice([1, 2, 3, 8, 16, 64, 256]))
+        T = int(rng.integers(0, 20000))
+        alpha = float(rng.choice([0.1, 1e-3, 0.37, 2.0 ** -7]))
+        bias = (rng.standard_normal(E) * rng.choice([1e-3, 1.0, 30.0])).astype(np.float32)
+        counts = rng.multinomial(T, rng.dirichlet(np.ones(E) * 0.3)) if E > 1 else np.array([T])
+        expert_bias = torch.from_numpy(bias.copy())
+        expert_count = torch.zeros(E)
+        expert_count += torch.from_numpy(counts.astype(np.int64)).float()
+        mean_count = expert_count.mean()
+        expert_bias.data += alpha * (mean_count - expert_count)
+        got = O.expert_bias_update(bias, counts, alpha=alpha)
+        assert np.array_equal(got, expert_bias.numpy().astype(np.float64)), (trial, E, T, alpha)
