@@ -2,7 +2,11 @@
 """Throughput of one MoE layer (route -> capacity dispatch -> expert FFN ->
 combine, plus the ledger) on one MI355X, through the C ABI of libmoe.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--mode graph]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--mode graph]
+
+The default workload is the largest that fits one GPU: the DeepSeek-V3-shaped
+layer (T 4096, h 7168, 256 experts, top-8, F 2048, 15 GB of expert weights).
+--config 1..5 selects another.
 
 A step is one pass of the whole path over one batch of tokens: moe_route,
 moe_dispatch (routing metadata), moe_expert_ffn_rows (the expert FFN, whose
@@ -17,7 +21,9 @@ the step ends.  The host decodes every step's ledger (moe_ledger_finalize,
 into buffers allocated once) a few steps behind the device, while later
 steps run.  Inputs are resident in HBM.
 So that the 256 MB last-level cache cannot serve the weights, successive steps
-rotate over several copies of x and of all weights (>= 1 GiB in total).
+rotate over several copies of x and of all weights (>= 1 GiB in total; one
+copy when a single set is larger).  A plain device-to-device copy is timed in
+the same run, as the practical HBM rate beside the published peak.
 
 Modes: "eager" (default) issues the pre-marshalled C calls every step;
 "graph" captures each rotation's step once into a HIP graph and replays it
@@ -50,10 +56,11 @@ FP32_PEAK_TFLOPS = 157.3
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=500)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", type=int, default=2,
-                   help="workload id (2 = the Switch-Base-shaped layer, the headline)")
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=4,
+                   help="workload id (4 = the DeepSeek-V3-shaped layer, the largest that "
+                        "fits one GPU: the headline)")
     p.add_argument("--mode", choices=["graph", "eager"], default="eager")
     p.add_argument("--weights", choices=["packed", "rowmajor"], default="packed",
                    help="expert weights in the packed fragment layout (packed once at setup, "
@@ -71,8 +78,9 @@ def parse():
     p.add_argument("--no-next-rows", action="store_true",
                    help="skip the timings of the entry points beyond the layer step (bias "
                         "update, FP8 payload, routing scenarios), e.g. under a profiler")
-    p.add_argument("--cpu-seconds", type=float, default=15.0,
-                   help="rough budget of the CPU-oracle baseline")
+    p.add_argument("--cpu-experts", type=int, default=16,
+                   help="experts whose FFN the CPU-oracle baseline runs (evenly spaced; the "
+                        "FFN time is scaled to all accepted rows)")
     return p.parse_args()
 
 
@@ -189,33 +197,128 @@ def committed_traffic(kernel, workload):
     return None
 
 
-def cpu_baseline(wl, inp, budget_s):
-    """The oracle as it stands, on the host cores: the whole layer of the same
-    workload (route -> dispatch -> FFN -> combine, float64), timed per pass."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, inp, n_experts):
+    """The oracle as it stands (float64 numpy, Python loops for slotting and
+    the ledger) on the host cores, on a bounded sample of the same workload:
+    router, top-k, capacity slotting, dispatch and combine over every token;
+    the expert FFN over the accepted rows of `n_experts` evenly spaced
+    experts, its time scaled by all accepted rows / the sampled rows; the
+    ledger timed on its own.  One warm-up pass, then three timed passes; the
+    median pass gives tokens/s.  Expert weights are widened to float64 on the
+    host once, before timing (the oracle takes float64 host arrays)."""
+    import numpy as np
     import oracle as O
     import moe_workloads as W
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        blas = None
+    cores = len(os.sched_getaffinity(0))
     x, wg = W.host_f64(inp.x), W.host_f64(inp.w_gate)
-    w1, b1, w2, b2 = (W.host_f64(t) for t in (inp.w1, inp.b1, inp.w2, inp.b2))
+    b1, b2 = W.host_f64(inp.b1), W.host_f64(inp.b2)
     bias = None if inp.logit_bias is None else inp.logit_bias.cpu().numpy()
+    src, owner = inp.src_rank.cpu().numpy(), inp.owner_rank.cpu().numpy()
     h_round = "bf16" if wl.dtype == "bf16" else "f32"
-    times = []
-    t_start = time.perf_counter()
-    while True:
+    n_experts = max(1, min(n_experts, wl.E))
+    sample = sorted({int(i * wl.E // n_experts) for i in range(n_experts)})
+    w1 = {e: W.host_f64(inp.w1[e]) for e in sample}
+    w2 = {e: W.host_f64(inp.w2[e]) for e in sample}
+
+    def one_pass():
+        t = {}
         t0 = time.perf_counter()
-        O.moe_layer(x, wg, w1, b1, w2, b2, wl.K, wl.cf, logit_bias=bias, h_round=h_round)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 5:
-            break
-    med = statistics.median(times)
-    return {"value": wl.T / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(times)} full passes of the {wl.name} layer ({wl.T} tokens; "
-                      f"route, dispatch, FFN, combine), float64 oracle, median {med:.3f} s "
-                      f"per pass"}
+        logits = O.router_logits(x, wg)
+        idx, gate = O.topk_softmax(logits, wl.K, bias)
+        t["route"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        cap = O.capacity(wl.T * wl.K, wl.E, wl.cf)
+        sl = O.slot_routes(idx, wl.E, cap)
+        xd = O.dispatch(x, sl["row_token"])
+        t["dispatch"] = time.perf_counter() - t0
+        off = sl["expert_offsets"]
+        rows = 0
+        Y = np.zeros((sl["R"], wl.h))
+        t0 = time.perf_counter()
+        for e in sample:
+            lo, hi = int(off[e]), int(off[e + 1])
+            if hi > lo:
+                _, Y[lo:hi] = O.expert_ffn_segment(xd[lo:hi], w1[e], b1[e], w2[e], b2[e],
+                                                   h_round)
+                rows += hi - lo
+        t["ffn_sample"] = time.perf_counter() - t0
+        t["ffn"] = t["ffn_sample"] * sl["R"] / max(rows, 1)
+        t0 = time.perf_counter()
+        O.combine(Y, sl["route_row"], gate)
+        t["combine"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.ledger(idx, gate, sl["route_row"], cap, src, owner, wl.n_ep, wl.h,
+                 wl.bytes_per_elem)
+        t["ledger"] = time.perf_counter() - t0
+        t["layer"] = t["route"] + t["dispatch"] + t["ffn"] + t["combine"]
+        return t, rows, sl["R"]
+
+    one_pass()  # warm-up
+    passes = [one_pass() for _ in range(3)]
+    layer = sorted(passes, key=lambda p: p[0]["layer"])[1]
+    t, rows, R = layer
+    return {"value": wl.T / t["layer"], "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "blas_threads": blas,
+            "stage_s": {k: round(v, 4) for k, v in t.items()},
+            "ledger_tokens_per_s": wl.T / t["ledger"],
+            "sample": f"{wl.name}, all {wl.T} tokens through the router, top-k, slotting, "
+                      f"dispatch and combine; the expert FFN of {len(sample)} of {wl.E} "
+                      f"experts ({rows} of {R} accepted rows), its time scaled by {R}/{rows}; "
+                      f"float64 oracle; 1 warm-up + 3 timed passes, median pass "
+                      f"{t['layer']:.3f} s; ledger timed separately ({t['ledger']:.3f} s)"}
+
+
+def stream_copy_gbs(torch, nbytes=2 << 30, reps=10):
+    """Read + write GB/s of a plain device-to-device copy (torch's copy
+    kernel) of `nbytes`, median of `reps` HIP-event-timed copies: the
+    practical HBM rate of this machine, reported beside the published peak."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del a, b
+    return 2 * nbytes / statistics.median(ts) / 1e9
+
+
+def step_plan(bufs, weights, inp, wl, main, packed, ledger_ws=None, side=None,
+              ledger_stream="fused", gather="ffn"):
+    """The LayerPlan of one benchmarked step: `weights` = (x, w_gate,
+    logit_bias, w1, b1, w2, b2), w1 / w2 packed when `packed`.  The defaults
+    are the benchmarked configuration (tests build the same plan)."""
+    from expert_dispatch_combine_amd.runner import LayerPlan
+    return LayerPlan(bufs, *weights, inp.src_rank, inp.owner_rank, wl.n_ep, 0.01, main=main,
+                     side=side, ledger_ws=ledger_ws, packed=packed,
+                     fused_tail=ledger_stream == "fused", gather_in_ffn=gather == "ffn")
+
+
+def _pct(v, q):
+    v = sorted(v)
+    i = min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))
+    return v[i]
 
 
 def main():
@@ -229,12 +332,13 @@ def main():
     import torch
     import moe_workloads as W
     import expert_dispatch_combine_amd as M
-    from expert_dispatch_combine_amd.runner import (LayerBuffers, LayerPlan, capacity_of,
-                                                    cfg_from, pack_weights)
+    from expert_dispatch_combine_amd.runner import (LayerBuffers, capacity_of, cfg_from,
+                                                    pack_weights)
 
     M.load_library()
     wl = W.CONFIGS[args.config]
     torch.cuda.set_device(0)
+    copy_gbs = stream_copy_gbs(torch)
     inp = W.make_inputs(wl, "cuda")
     mc = cfg_from(wl)
     cap = capacity_of(mc)
@@ -258,17 +362,19 @@ def main():
     main_s = torch.cuda.Stream()
     side_s = torch.cuda.Stream() if args.ledger_stream == "side" else None
     ledger_ws = torch.empty_like(bufs.ws)
-    plans = [LayerPlan(bufs, *st, inp.src_rank, inp.owner_rank, wl.n_ep, 0.01, main=main_s,
-                       side=side_s, ledger_ws=ledger_ws, packed=packed,
-                       fused_tail=args.ledger_stream == "fused",
-                       gather_in_ffn=args.gather == "ffn") for st in sets]
+    # at least 5 plans (each with its own host stage), so that the host can
+    # decode a step's ledger while the next four are queued, also when one
+    # rotation set is all there is
+    n_plans = max(n_rot, 5)
+    plans = [step_plan(bufs, sets[i % n_rot], inp, wl, main_s, packed, ledger_ws, side_s,
+                       args.ledger_stream, args.gather) for i in range(n_plans)]
     torch.cuda.synchronize()
-    done = [torch.cuda.Event() for _ in range(n_rot)]
+    done = [torch.cuda.Event() for _ in range(n_plans)]
 
     # eager warm-up (also before any capture)
     with torch.cuda.stream(main_s):
-        for i in range(max(args.warmup, n_rot)):
-            plans[i % n_rot].launch()
+        for i in range(max(args.warmup, n_plans)):
+            plans[i % n_plans].launch()
     torch.cuda.synchronize()
     led = plans[0].ledger()
 
@@ -283,21 +389,20 @@ def main():
         torch.cuda.synchronize()
         with torch.cuda.stream(main_s):
             for i in range(args.warmup):
-                graphs[i % n_rot].replay()
+                graphs[i % n_plans].replay()
         torch.cuda.synchronize()
 
     # The host decodes step i-lag's ledger (C moe_ledger_finalize into the
     # plan's buffers) after issuing step i, so up to `lag` later steps stay
     # queued on the device while it does.  A plan's stage is rewritten only
-    # when the plan is launched again, n_rot steps later, so lag < n_rot (with
-    # a single rotation set each step is decoded before the next is issued).
-    lag = min(4, n_rot - 1)
+    # when the plan is launched again, n_plans steps later, so lag < n_plans.
+    lag = min(4, n_plans - 1)
 
     def run_steps(K, events=None):
         pending = []
         with torch.cuda.stream(main_s):
             for i in range(K):
-                j = i % n_rot
+                j = i % n_plans
                 if graphs is not None and events is None:
                     graphs[j].replay()
                 else:
@@ -329,9 +434,13 @@ def main():
     torch.cuda.synchronize()
     elapsed_eager = time.perf_counter() - t1
 
-    def mean_ms(a, b):
-        return statistics.fmean(evs[i][a].elapsed_time(evs[i][b]) for i in range(K))
+    def per_step_ms(a, b):
+        return [evs[i][a].elapsed_time(evs[i][b]) for i in range(K)]
 
+    def mean_ms(a, b):
+        return statistics.fmean(per_step_ms(a, b))
+
+    step_ms = per_step_ms(0, 4)
     t_route, t_disp, t_ffn, t_comb = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3), mean_ms(3, 4)
     R = int(led["accepted_routes"])
     offs = bufs.expert_offsets.cpu().tolist()
@@ -351,14 +460,21 @@ def main():
     roof["traffic"] = committed_traffic("expert_ffn", wl.name) if packed else None
     roof.update({
         "kernel": "expert FFN grouped GEMM: the two launches (GEMM1, GEMM2) of one "
-                  "moe_expert_ffn, timed together",
+                  "moe_expert_ffn_rows, timed together",
         "algorithmic_bytes": alg["ffn_bytes"], "algorithmic_flops": alg["ffn_flops"],
         "arithmetic_intensity": ai, "mfma_util": alg["ffn_flops"] / ffn_s / 1e12 / peak_flops,
         "avg_ms": t_ffn,
+        "frac_of_measured_copy": (alg["ffn_bytes"] / ffn_s / 1e9 / copy_gbs
+                                  if ai < ridge else None),
     })
     if roof["traffic"] is not None:
         roof["traffic_over_algorithmic"] = roof["traffic"] / alg["ffn_bytes"]
 
+    def hbm(nbytes, ms):
+        return {"ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+    tail = "combine_ledger" if args.ledger_stream == "fused" else "combine"
     res = {
         "metric": BASELINE_METRIC,
         "value": wl.T * K / elapsed,
@@ -381,9 +497,17 @@ def main():
         "routes_per_s": wl.A * K / elapsed,
         "accepted_routes_per_s": R * K / elapsed,
         "eager_tokens_per_s": wl.T * K / elapsed_eager,
-        "per_call_ms": {"route": t_route, "dispatch": t_disp, "expert_ffn": t_ffn,
-                        ("combine_ledger" if args.ledger_stream == "fused" else "combine"):
-                        t_comb},
+        "step_ms": {"median": statistics.median(step_ms), "p10": _pct(step_ms, 0.1),
+                    "p90": _pct(step_ms, 0.9), "source": "HIP events around each step of "
+                    "the eager pass (device time, launches included)"},
+        "per_call_ms": {"route": t_route, "dispatch": t_disp, "expert_ffn": t_ffn, tail: t_comb},
+        "per_call_hbm": {"route": hbm(alg["route_bytes"], t_route),
+                         "dispatch_metadata" if args.gather == "ffn" else "dispatch":
+                         hbm(alg["dispatch_bytes"] - (2 * R * wl.h * wl.bytes_per_elem
+                                                      if args.gather == "ffn" else 0), t_disp),
+                         "expert_ffn": hbm(alg["ffn_bytes"], t_ffn),
+                         tail: hbm(alg["combine_bytes"], t_comb)},
+        "hbm_copy_gbs": copy_gbs,
         "roofline": roof,
         "ledger": {k: led[k] for k in ("accepted_routes", "overflow", "balance_ratio",
                                         "local_hit_ratio", "l_aux")},
@@ -391,8 +515,9 @@ def main():
     if not args.no_next_rows:
         res["next_rows"] = next_rows(M, bufs, torch, main_s, inp.x)
         res["next_rows"]["routing_scenarios"] = routing_scenarios(M, W, torch, main_s)
+    del plans, sets
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, inp,
-                                                                         args.cpu_seconds)
+                                                                         args.cpu_experts)
     print(json.dumps(res), flush=True)
 
 

@@ -58,7 +58,7 @@ import numpy as np
 __all__ = [
     "round_bf16", "round_f32", "router_logits", "add_logit_bias", "topk_softmax",
     "expert_loads", "capacity", "overflow", "slot_routes", "dispatch",
-    "gelu_tanh", "expert_ffn", "expert_ffn_rows", "combine", "combine_index_add",
+    "gelu_tanh", "expert_ffn_segment", "expert_ffn", "expert_ffn_rows", "combine", "combine_index_add",
     "summarize_routes", "dispatch_locality", "aux_loss_terms",
     "uniform_expert_placement", "load_monitor", "ledger", "moe_layer",
     "moe_layer_per_token", "routes_from_idx", "top1_counts", "expert_bias_update",
@@ -255,28 +255,36 @@ def _round_h(H, h_round):
     raise ValueError(h_round)
 
 
-def expert_ffn(xd, offsets, w1, b1, w2, b2, h_round: Optional[str] = None):
-    """Each expert's FFN over its own rows [offsets[e], offsets[e+1]).
+def expert_ffn_segment(rows_x, w1_e, b1_e, w2_e, b2_e, h_round: Optional[str] = None):
+    """One expert's FFN ([DSV3] section 一) on a block of its rows:
+    H = GELU_tanh(rows_x W1_e^T + b1_e), rounded to `h_round` ("bf16" on bf16
+    workloads: H is the bf16 operand of the second product); Y = H W2_e^T +
+    b2_e rounded to fp32.  W1_e is [F, h], W2_e is [h, F] (reading R7).
+    Returns (H, Y) as float64 arrays."""
+    xe = np.asarray(rows_x, dtype=np.float64)
+    u = xe @ np.asarray(w1_e, np.float64).T + np.asarray(b1_e, np.float64)
+    H = _round_h(gelu_tanh(u), h_round)
+    Y = round_f32(H @ np.asarray(w2_e, np.float64).T + np.asarray(b2_e, np.float64))
+    return H, Y
 
-    H = GELU_tanh(xd W1_e^T + b1_e), rounded to `h_round` ("bf16" on bf16
-    workloads: H is the bf16 operand of the second product); Y = H W2_e^T + b2_e
-    rounded to fp32.  Reading R7.  Returns (H, Y) as float64 arrays.
-    """
+
+def expert_ffn(xd, offsets, w1, b1, w2, b2, h_round: Optional[str] = None):
+    """Each expert's FFN over its own rows [offsets[e], offsets[e+1]), by
+    `expert_ffn_segment`.  Reading R7.  Returns (H, Y) as float64 arrays.
+    `w1`, `w2`, `b1`, `b2` are indexed by expert (arrays, or any sequence
+    that yields one expert's weights at a time)."""
     xd = np.asarray(xd, dtype=np.float64)
     E = len(offsets) - 1
     R = int(offsets[E])
-    F = np.asarray(w1).shape[1]
-    h = np.asarray(w2).shape[1]
+    F = np.asarray(w1[0]).shape[0]
+    h = np.asarray(w2[0]).shape[0]
     H = np.zeros((R, F))
     Y = np.zeros((R, h))
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
             continue
-        u = xd[lo:hi] @ np.asarray(w1[e], np.float64).T + np.asarray(b1[e], np.float64)
-        H[lo:hi] = _round_h(gelu_tanh(u), h_round)
-        Y[lo:hi] = round_f32(H[lo:hi] @ np.asarray(w2[e], np.float64).T
-                             + np.asarray(b2[e], np.float64))
+        H[lo:hi], Y[lo:hi] = expert_ffn_segment(xd[lo:hi], w1[e], b1[e], w2[e], b2[e], h_round)
     return H, Y
 
 

@@ -20,7 +20,8 @@ import expert_dispatch_combine_amd as M
 import moe_workloads as W
 import oracle as O
 from expert_dispatch_combine_amd.runner import LayerBuffers, pack_weights
-from gpu_util import (U32, banner, bias_np, custom_inputs, device_inputs, host, rms, to_dev)
+from gpu_util import (U32, banner, bias_np, check_ffn_segment, custom_inputs, device_inputs,
+                      host, host_expert, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +58,8 @@ def _run_ffn(inp: W.Inputs, cap, sl, packed=False):
 
 
 def _check_rows(inp, sl, b, rows):
-    """Compare H and Y of the given dispatched rows with the oracle's."""
+    """Compare H and Y of the given dispatched rows with the oracle's
+    (O.expert_ffn_segment per expert, bounds in gpu_util.check_ffn_segment)."""
     cfg = inp.cfg
     if len(rows) == 0:
         return
@@ -69,27 +71,8 @@ def _check_rows(inp, sl, b, rows):
     Yg = b.y[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
     for e in np.unique(experts):
         m = experts == e
-        w1 = host(inp.w1[int(e)])
-        w2 = host(inp.w2[int(e)])
-        b1 = host(inp.b1[int(e)])
-        b2 = host(inp.b2[int(e)])
-        xe = x64[m]
-        u = xe @ w1.T + b1
-        H = O.gelu_tanh(u)
-        H = O.round_bf16(H) if h_round == "bf16" else O.round_f32(H)
-        Y = O.round_f32(H @ w2.T + b2)
-        du = cfg.h * U32 * (np.abs(xe) @ np.abs(w1).T) + U32 * np.abs(u)
-        ulp = 2.0 ** -7 if h_round == "bf16" else 2.0 ** -23
-        tolH = ulp * np.abs(H) + 1.13 * du + 1e-6
-        dH = np.abs(Hg[m] - H)
-        assert np.all(dH <= tolH), float((dH - tolH).max())
-        if h_round == "bf16":
-            assert np.mean(dH > 0) < 0.02
-        tolY = (ulp * np.abs(H) + 1.13 * du) @ np.abs(w2).T \
-            + cfg.F * U32 * (np.abs(H) @ np.abs(w2).T) + U32 * np.abs(Y) + 1e-6
-        dY = np.abs(Yg[m] - Y)
-        assert np.all(dY <= tolY), float((dY - tolY).max())
-        assert rms(Yg[m] - Y) <= 2.0 ** -8 * rms(Y) + 1e-7
+        check_ffn_segment(h_round, x64[m], host_expert(inp.w1, e), host_expert(inp.b1, e),
+                          host_expert(inp.w2, e), host_expert(inp.b2, e), Hg[m], Yg[m])
 
 
 @pytest.mark.parametrize("cid,packed", [(1, False), (2, False), (2, True), (5, False),
@@ -102,27 +85,18 @@ def test_ffn_full_on_workloads(cid, packed):
     _check_rows(inp, sl, b, np.arange(sl["R"]))
 
 
-@pytest.mark.parametrize("cid,packed", [(3, False), (3, True), (4, False), (4, True)])
-def test_ffn_sampled_rows_full_size(cid, packed):
-    """Full-size workloads, launched exactly as the layer launches them;
-    a sample of rows (every expert's first and last row, plus random rows)
-    is checked against the oracle row by row."""
-    banner(f"ffn sampled config {cid} packed={packed}")
+@pytest.mark.parametrize("cid", [3, 4])
+def test_ffn_every_row_full_size(cid):
+    """Full-size workloads on row-major weights and x_disp, launched exactly as
+    the layer launches them; every accepted row of both GEMMs against the
+    oracle, one expert's weights on the host at a time.  (The packed weights
+    with the rows gathered inside the first GEMM, the benchmarked path, are
+    checked the same way in test_gpu_bench_step.)"""
+    banner(f"ffn every row config {cid}")
     inp = device_inputs(cid)
     _, _, cap, sl = _oracle_dispatch(inp)
-    b = _run_ffn(inp, cap, sl, packed)
-    offs = sl["expert_offsets"]
-    rng = np.random.default_rng(cid)
-    rows = set()
-    for e in range(inp.cfg.E):
-        if offs[e + 1] > offs[e]:
-            rows.update({int(offs[e]), int(offs[e + 1] - 1)})
-    rows.update(rng.integers(0, sl["R"], 48).tolist())
-    rows = np.array(sorted(rows))
-    if cid == 4:  # 256 experts: keep the per-expert weight copies bounded
-        rows = rows[rng.permutation(len(rows))[:96]]
-        rows.sort()
-    _check_rows(inp, sl, b, rows)
+    b = _run_ffn(inp, cap, sl, False)
+    _check_rows(inp, sl, b, np.arange(sl["R"]))
 
 
 @pytest.mark.parametrize("packed", [False, True])
@@ -170,6 +144,7 @@ def test_ffn_ragged_segments(T, h, E, K, F, cf, packed):
     (None, (513, 64, 64, 6, 128, 1.0), True),              # many small / empty experts
     (None, (2500, 192, 3, 1, 448, 1.5), True),             # long segments: tiled kernel
     (None, (4096, 256, 4, 1, 512, 1.0), False),            # wide kernel, 256 x 256 tiles
+    (None, (4096, 256, 4, 1, 512, 1.0), True),             # the same, packed weights
     (None, (3000, 128, 4, 1, 384, 1.3), True),             # wide kernel, 128 x 128 tiles
     (None, (1, 64, 1, 1, 64, 1.0), False),
     (1, None, False)])                                      # fp32: rows copied into y first
@@ -250,7 +225,7 @@ def test_combine(T, K, h, R, drop):
     _check_combine(T, K, h, R, drop, seed=T + h)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 4, 5])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
 def test_combine_on_workload_routing(cid):
     """Combine with the workload's own routing and oracle expert outputs."""
     banner(f"combine config {cid}")

@@ -22,8 +22,8 @@ import expert_dispatch_combine_amd as M
 import moe_workloads as W
 import oracle as O
 from expert_dispatch_combine_amd.runner import LayerBuffers, run_layer
-from gpu_util import (banner, bias_np, buffers_for, custom_inputs, device_inputs, host,
-                      near_tie_tokens, rms, to_dev)
+from gpu_util import (banner, bias_np, buffers_for, compare_ledger, custom_inputs,
+                      device_inputs, host, near_tie_tokens, rms, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,33 +46,7 @@ def _gpu_ledger(cfg, idx, gate, route_row, cap, src, owner, n_ep, alpha=0.01, **
                         to_dev(owner, torch.int32), n_ep, alpha, ws, **kw)
 
 
-INT_FIELDS = ["total_tokens", "total_routes", "capacity", "accepted_routes", "overflow",
-              "max_load", "logical_route_bytes", "all_to_all_bytes", "accepted_route_bytes",
-              "local_routes", "cross_rank_routes", "cross_rank_dispatch_bytes",
-              "cross_rank_roundtrip_bytes", "accepted_local_routes",
-              "accepted_cross_rank_routes", "accepted_cross_rank_dispatch_bytes",
-              "accepted_cross_rank_roundtrip_bytes"]
-EXACT_FLOATS = ["balance_ratio", "local_hit_ratio", "accepted_local_hit_ratio",
-                "pair_bytes_uniform"]
-
-
-def _compare_ledger(g, o):
-    for k in INT_FIELDS:
-        assert g[k] == o[k], (k, g[k], o[k])
-    for k in EXACT_FLOATS:
-        assert g[k] == o[k], (k, g[k], o[k])
-    assert g["loads"] == [int(v) for v in o["expert_loads"]]
-    assert np.array_equal(np.array(g["f"]), o["f"])
-    T = max(o["total_tokens"], 1)
-    dP = np.asarray(o["expert_loads"], np.float64) * 2.0 ** -33 / T + 1e-15 * np.abs(o["P"])
-    assert np.all(np.abs(np.array(g["P"]) - o["P"]) <= dP)
-    d_aux = g["alpha"] * float(np.sum(np.asarray(o["f"]) * dP)) + 1e-15 * abs(o["l_aux"])
-    assert abs(g["l_aux"] - o["l_aux"]) <= d_aux
-    scale = o["num_experts"] / max(o["total_routes"] / T, 1)  # E / K
-    assert abs(g["l_aux_norm"] - o["l_aux_norm"]) <= scale * d_aux + 1e-15 * abs(o["l_aux_norm"])
-    np.testing.assert_allclose(g["load_var_over_mean"], o["load_var_over_mean"], rtol=1e-12)
-    assert bool(g["imbalanced"]) == o["imbalanced"]
-    assert np.array_equal(np.array(g["pair_routes"]), o["pair_routes"])
+_compare_ledger = compare_ledger
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])

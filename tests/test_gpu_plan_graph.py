@@ -31,7 +31,8 @@ def _same(a, c):
 @pytest.mark.parametrize("cid,packed,tail,gather", [
     (1, False, "side", False), (2, False, "side", False), (2, True, "side", False),
     (3, True, "side", False), (4, True, "side", False), (5, True, "side", False),
-    (1, False, "fused", True), (2, True, "fused", True), (4, True, "fused", True),
+    (1, False, "fused", True), (2, True, "fused", True), (3, True, "fused", True),
+    (4, True, "fused", True),
     (5, True, "fused", True)])
 def test_plan_and_graph_replay_match_eager(cid, packed, tail, gather):
     """tail "side": the ledger on a second stream beside the FFN; "fused":
