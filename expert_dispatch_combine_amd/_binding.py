@@ -23,6 +23,7 @@ EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_capacity", "moe_max_rows", "moe_workspace_bytes",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_ledger",
     "moe_ledger_stage_bytes", "moe_ledger_launch", "moe_ledger_finalize",
+    "moe_dispatch_noalloc",
     "moe_expert_ffn_packed", "moe_pack_expert_weights", "moe_bias_update",
     "moe_fp8_scale", "moe_dispatch_fp8", "moe_fp8_dequantize", "moe_recommend_plan",
     "moe_combine_ledger", "moe_expert_ffn_rows",
@@ -98,6 +99,8 @@ def load_library():
     lib.moe_route.argtypes = [cfgp, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_dispatch.restype = ctypes.c_int
     lib.moe_dispatch.argtypes = [cfgp, P, P, _I64, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_dispatch_noalloc.restype = ctypes.c_int
+    lib.moe_dispatch_noalloc.argtypes = [cfgp, P, P, _I64, P, P, P, P, P, P, P]
     lib.moe_expert_ffn.restype = ctypes.c_int
     lib.moe_expert_ffn.argtypes = [cfgp, _I64, P, P, P, P, P, P, P, P, P]
     lib.moe_combine.restype = ctypes.c_int
@@ -262,6 +265,22 @@ def moe_fp8_dequantize(cfg: MoeCfg, capacity: int, x_disp_q, scale, expert_offse
                                 _ptr(expert_offsets, "i32", cfg, "expert_offsets"),
                                 _ptr(x_disp, "act", cfg, "x_disp"), _stream(stream))
     _check("moe_fp8_dequantize", st)
+
+
+def moe_dispatch_noalloc(cfg: MoeCfg, x, topk_idx, capacity: int, expert_offsets, route_rank,
+                         route_row, row_token, x_disp, expert_load=None, stream=None) -> None:
+    """moe_dispatch with its scratch in the library's static device array (no
+    workspace argument, nothing allocated); see include/moe.h."""
+    lib = load_library()
+    st = lib.moe_dispatch_noalloc(ctypes.byref(cfg), _ptr(x, "act", cfg, "x"),
+                                  _ptr(topk_idx, "i32", cfg, "topk_idx"), int(capacity),
+                                  _ptr(expert_offsets, "i32", cfg, "expert_offsets"),
+                                  _ptr(route_rank, "i32", cfg, "route_rank"),
+                                  _ptr(route_row, "i32", cfg, "route_row"),
+                                  _ptr(row_token, "i32", cfg, "row_token"),
+                                  _ptr(x_disp, "act", cfg, "x_disp"),
+                                  _ptr(expert_load, "i32", cfg, "expert_load"), _stream(stream))
+    _check("moe_dispatch_noalloc", st)
 
 
 def moe_dispatch(cfg: MoeCfg, x, topk_idx, capacity: int, expert_offsets, route_rank,

@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "moe.h"
@@ -138,6 +139,64 @@ int moe_dispatch(const moe_cfg* cfg, const void* x, const int32_t* topk_idx, int
   if (rmax > 0 && (!row_token || (x_disp && !x))) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < moe_workspace_bytes(cfg)) return MOE_ERR_SHAPE;
   const int64_t row_bytes = (int64_t)cfg->h * elem_bytes(cfg);
+  return hip_status(launch_dispatch(x, topk_idx, A, cfg->K, cfg->E, capacity, row_bytes, rmax,
+                                    expert_offsets, route_rank, route_row, row_token, x_disp,
+                                    expert_load, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-alloc
+// Scratch of moe_dispatch_noalloc: the per-block expert counts of the
+// counting dispatch (launch_dispatch's workspace), in a static device array
+// instead of a caller workspace.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels receive the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on the first call there.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, or nullptr on a HIP error.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int moe_dispatch_noalloc(const moe_cfg* cfg, const void* x, const int32_t* topk_idx,
+                         int64_t capacity, int32_t* expert_offsets, int32_t* route_rank,
+                         int32_t* route_row, int32_t* row_token, void* x_disp,
+                         int32_t* expert_load, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  const int64_t A = routes_of(cfg);
+  const int64_t rmax = rows_max(cfg, capacity);
+  if (!expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (A > 0 && (!topk_idx || !route_rank || !route_row)) return MOE_ERR_INVALID_ARG;
+  if (rmax > 0 && (!row_token || (x_disp && !x))) return MOE_ERR_INVALID_ARG;
+  // the counts the dispatch keeps between its kernels must fit the array
+  if (dispatch_ws_bytes(A, cfg->E) > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return MOE_ERR_UNSUPPORTED;
+  void* ws = scratch_ptr();
+  if (!ws) return MOE_ERR_HIP;
+  const int64_t row_bytes = (int64_t)cfg->h * elem_bytes(cfg);
+  // every count the kernels read is written by them first in the same call,
+  // so the array needs no clearing between calls
   return hip_status(launch_dispatch(x, topk_idx, A, cfg->K, cfg->E, capacity, row_bytes, rmax,
                                     expert_offsets, route_rank, route_row, row_token, x_disp,
                                     expert_load, ws, (hipStream_t)stream));

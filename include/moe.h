@@ -202,6 +202,26 @@ int moe_dispatch(const moe_cfg* cfg, const void* x, const int32_t* topk_idx,
                  int32_t* route_row, int32_t* row_token, void* x_disp,
                  int32_t* expert_load, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_dispatch for callers that cannot allocate memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same arguments and results as moe_dispatch, without the workspace: the
+ * dispatch's scratch (the per-block expert counts, ceil(T*K/1024) * (E+1)
+ * int32) lives in a static device array of MOE_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends.  Allocates
+ * nothing (no hipMalloc, no allocating library call).  Returns
+ * MOE_ERR_UNSUPPORTED, before enqueuing anything, when that scratch would
+ * exceed the array: ceil(T*K/1024) * (E+1) * 4 bytes, rounded up to 256,
+ * above MOE_NOALLOC_SCRATCH_BYTES (4 MiB), e.g. more than 1,047,552 routes at
+ * E = 1024 or 16,518,144 at E = 64.  Every call on one
+ * GPU shares the array: calls that overlap on one GPU (on different streams
+ * or host threads) race on it and may give wrong results; calls in order on
+ * one stream are safe.  `stream` must belong to the current device. */
+#define MOE_NOALLOC_SCRATCH_BYTES (4 << 20)
+int moe_dispatch_noalloc(const moe_cfg* cfg, const void* x, const int32_t* topk_idx,
+                         int64_t capacity, int32_t* expert_offsets, int32_t* route_rank,
+                         int32_t* route_row, int32_t* row_token, void* x_disp,
+                         int32_t* expert_load, void* stream);
+
 /* Expert FFN over ragged expert segments ([DSV3] section 一
  * FFN(x) = W2 GELU(W1 x + b1) + b2, GELU in its tanh form):
  * for each expert e and row r in [offset[e], offset[e+1]):

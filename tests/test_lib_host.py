@@ -228,3 +228,22 @@ def test_finalize_rejects_a_stage_without_a_ledger(lib):
     import torch
     with pytest.raises(M.MoeError):
         M.moe_ledger_finalize(cfg, 8, n_ep, 0.01, torch.zeros(nbytes, dtype=torch.uint8))
+
+
+def test_noalloc_dispatch_checks_on_the_host(lib):
+    """moe_dispatch_noalloc rejects, before any HIP call, arguments that are
+    invalid and sizes whose counting scratch (ceil(T*K/1024) * (E+1) int32,
+    rounded up to 256 bytes) exceeds its 4 MiB static array."""
+    fake = ctypes.c_void_p(256)
+    assert lib.moe_dispatch_noalloc(None, fake, fake, 8, fake, fake, fake, fake, None, None,
+                                    None) == 1
+    cfg = M.MoeCfg.make(2048, 64, 1024, 1, 64, "bf16", 1.0)
+    assert lib.moe_dispatch_noalloc(ctypes.byref(cfg), fake, fake, -1, fake, fake, fake, fake,
+                                    None, None, None) == 1
+    assert lib.moe_dispatch_noalloc(ctypes.byref(cfg), fake, fake, 8, None, fake, fake, fake,
+                                    None, None, None) == 1
+    # one route more than the largest batch that fits, at E = 1024 and E = 64
+    for E, A_fit in ((1024, 1_047_552), (64, 16_518_144)):
+        cfg = M.MoeCfg.make(A_fit + 1, 64, E, 1, 64, "bf16", 1.0)
+        assert lib.moe_dispatch_noalloc(ctypes.byref(cfg), fake, fake, 8, fake, fake, fake, fake,
+                                        None, None, None) == 5, E
