@@ -97,27 +97,39 @@ def algorithmic(wl, R, E_nz):
     }
 
 
-def next_rows(M, bufs, torch, stream, x, reps=200):
+def next_rows(M, bufs, torch, stream, x, weights, wl, reps=50):
     """Per-call time (HIP events on `stream`, one pair per call, averaged; an
     upper bound that includes the launch) of the entry points beyond the
     layer step, on the step's own buffers: moe_bias_update (aux-loss-free
-    balancing) and the FP8 payload (moe_fp8_scale, moe_dispatch_fp8,
-    moe_fp8_dequantize), with the dispatch payload bytes of both formats."""
+    balancing) and the FP8 payload (moe_fp8_scale, moe_dispatch_fp8 and
+    moe_expert_ffn_fp8, whose first GEMM reads the E4M3 codes), with the
+    dispatch payload bytes of both formats and the FP8 expert FFN's
+    algorithmic bytes and HBM rate."""
     cfg, b = bufs.cfg, bufs
+    _, _, _, w1, b1, w2, b2 = weights
     bias = torch.zeros((cfg.E,), dtype=torch.float32, device="cuda")
     calls = {"bias_update_us": lambda: M.moe_bias_update(cfg, b.topk_idx, bias, 1e-3, None,
                                                          stream)}
     out = {}
+    packed = w1 is not None and wl.dtype == "bf16"
+    fp8_ffn = False
     if cfg.dtype == M.MOE_BF16:
         scale = torch.zeros((1,), dtype=torch.float32, device="cuda")
         xq = torch.empty((max(b.r_max, 1), cfg.h), dtype=torch.uint8, device="cuda")
-        xd = torch.empty_like(b.x_disp)
         calls["fp8_scale_us"] = lambda: M.moe_fp8_scale(cfg, x, scale, b.ws, stream)
         calls["fp8_dispatch_us"] = lambda: M.moe_dispatch_fp8(
             cfg, x, scale, b.topk_idx, b.capacity, b.expert_offsets, b.route_rank, b.route_row,
             b.row_token, xq, None, b.ws, stream)
-        calls["fp8_dequantize_us"] = lambda: M.moe_fp8_dequantize(
-            cfg, b.capacity, xq, scale, b.expert_offsets, xd, stream)
+        try:
+            M.moe_expert_ffn_fp8(cfg, b.capacity, xq, scale, b.expert_offsets, w1, b1, w2, b2,
+                                 b.h_buf, b.y, packed, stream)
+            fp8_ffn = True
+        except M.MoeError:  # a shape whose first GEMM reads bf16 only
+            pass
+        if fp8_ffn:
+            calls["fp8_expert_ffn_us"] = lambda: M.moe_expert_ffn_fp8(
+                cfg, b.capacity, xq, scale, b.expert_offsets, w1, b1, w2, b2, b.h_buf, b.y,
+                packed, stream)
         R = int(b.expert_offsets[-1].item())
         out["fp8_payload_bytes"] = R * cfg.h
         out["bf16_payload_bytes"] = R * cfg.h * 2
@@ -131,6 +143,16 @@ def next_rows(M, bufs, torch, stream, x, reps=200):
                 e.record(stream)
         torch.cuda.synchronize()
         out[name] = statistics.fmean(a.elapsed_time(e) for a, e in evs) * 1e3
+    if fp8_ffn:
+        offs = b.expert_offsets.cpu().tolist()
+        e_nz = sum(1 for e in range(wl.E) if offs[e + 1] > offs[e])
+        # the bf16 FFN's bytes with the rows read as one byte per element
+        nbytes = algorithmic(wl, R, e_nz)["ffn_bytes"] - R * cfg.h
+        gbs = nbytes / (out["fp8_expert_ffn_us"] * 1e-6) / 1e9
+        out["fp8_expert_ffn_roofline"] = {"bound": "hbm", "achieved": gbs,
+                                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                          "frac": gbs / HBM_PEAK_GBS,
+                                          "algorithmic_bytes": nbytes}
     return out
 
 
@@ -169,8 +191,50 @@ def routing_scenarios(M, W, torch, stream, reps=200):
                      "local_hit_ratio": led["local_hit_ratio"],
                      "cross_rank_dispatch_bytes": led["cross_rank_dispatch_bytes"],
                      "overflow": led["overflow"], "balance_ratio": led["balance_ratio"],
+                     "rank_balance": _rank_balance(led),
                      "plan": M.moe_recommend_plan(led)}
+        out[name]["locality_placement"] = placement_row(M, torch, b, inp.src_rank, cfg.n_ep,
+                                                        stream)
     return out
+
+
+def _rank_balance(led):
+    """max / mean of the accepted routes each rank's experts compute (the
+    ledger's rank-pair matrix summed over source ranks)."""
+    loads = [sum(col) for col in zip(*led["pair_routes"])]
+    mean = sum(loads) / len(loads)
+    return max(loads) / mean if mean else 0.0
+
+
+def placement_row(M, torch, b, src_rank, n_ep, stream):
+    """Locality-aware placement of the step's routing: the expert x
+    source-rank affinity on the GPU (moe_expert_rank_affinity), the placement
+    on the host (moe_place_experts), and the GPU ledger under it beside the
+    round-robin one: local hit ratio, cross-rank bytes, per-rank load balance
+    and the plan decision."""
+    cfg = b.cfg
+    aff = torch.empty((cfg.E, n_ep), dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        M.moe_expert_rank_affinity(cfg, b.topk_idx, None, src_rank, n_ep, aff, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    owner = M.moe_place_experts(aff.cpu(), n_ep)
+    t_place = time.perf_counter() - t0
+    rows = {}
+    for label, own in (("round_robin", [e % n_ep for e in range(cfg.E)]), ("placed", owner)):
+        led = M.moe_ledger(cfg, b.topk_idx, b.topk_gate, b.route_row, b.capacity, src_rank,
+                           torch.tensor(own, dtype=torch.int32, device="cuda"), n_ep, 0.01, b.ws,
+                           stream)
+        rows[label] = {"local_hit_ratio": led["local_hit_ratio"],
+                       "cross_rank_dispatch_bytes": led["cross_rank_dispatch_bytes"],
+                       "rank_balance": _rank_balance(led), "plan": M.moe_recommend_plan(led)}
+    rows["owner"] = owner
+    rows["affinity_us"] = e0.elapsed_time(e1) * 1e3
+    rows["placement_host_ms"] = t_place * 1e3
+    return rows
 
 
 def committed_traffic(kernel, workload):
@@ -513,7 +577,10 @@ def main():
                                         "local_hit_ratio", "l_aux")},
     }
     if not args.no_next_rows:
-        res["next_rows"] = next_rows(M, bufs, torch, main_s, inp.x)
+        res["next_rows"] = next_rows(M, bufs, torch, main_s, inp.x, sets[0], wl)
+        if wl.E % wl.n_ep == 0:
+            res["next_rows"]["locality_placement"] = placement_row(M, torch, bufs, inp.src_rank,
+                                                                   wl.n_ep, main_s)
         res["next_rows"]["routing_scenarios"] = routing_scenarios(M, W, torch, main_s)
     del plans, sets
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, inp,

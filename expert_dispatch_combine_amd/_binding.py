@@ -23,7 +23,8 @@ EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_capacity", "moe_max_rows", "moe_workspace_bytes",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_ledger",
     "moe_ledger_stage_bytes", "moe_ledger_launch", "moe_ledger_finalize",
-    "moe_dispatch_noalloc",
+    "moe_dispatch_noalloc", "moe_expert_rank_affinity", "moe_place_experts",
+    "moe_expert_ffn_fp8",
     "moe_expert_ffn_packed", "moe_pack_expert_weights", "moe_bias_update",
     "moe_fp8_scale", "moe_dispatch_fp8", "moe_fp8_dequantize", "moe_recommend_plan",
     "moe_combine_ledger", "moe_expert_ffn_rows",
@@ -135,6 +136,12 @@ def load_library():
     lib.moe_recommend_plan.restype = ctypes.c_int
     lib.moe_recommend_plan.argtypes = [ctypes.POINTER(MoeLedger), ctypes.POINTER(_F64),
                                        ctypes.c_int32]
+    lib.moe_expert_ffn_fp8.restype = ctypes.c_int
+    lib.moe_expert_ffn_fp8.argtypes = [cfgp, _I64, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P]
+    lib.moe_expert_rank_affinity.restype = ctypes.c_int
+    lib.moe_expert_rank_affinity.argtypes = [cfgp, P, P, P, ctypes.c_int32, P, P]
+    lib.moe_place_experts.restype = ctypes.c_int
+    lib.moe_place_experts.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P]
     lib.moe_fp8_dequantize.restype = ctypes.c_int
     lib.moe_fp8_dequantize.argtypes = [cfgp, _I64, P, P, P, P, P]
     _lib = lib
@@ -476,3 +483,47 @@ def moe_recommend_plan(ledger: dict, thresholds=None, use_locality: bool = True)
         raise MoeError("moe_recommend_plan", 1)
     return PLAN_NAMES[r]
 
+
+
+def moe_expert_ffn_fp8(cfg: MoeCfg, capacity: int, x_disp_q, scale, expert_offsets, w1, b1,
+                       w2, b2, h_buf, y, packed: bool = False, stream=None) -> None:
+    """The expert FFN on the E4M3 dispatch payload (x_disp_q uint8 [R_max, h],
+    scale fp32 [1] on the device); packed: w1/w2 in the packed layout."""
+    lib = load_library()
+    if not isinstance(x_disp_q, torch.Tensor) or x_disp_q.dtype != torch.uint8:
+        raise ValueError("x_disp_q: expected a uint8 device tensor")
+    if x_disp_q.device.type != "cuda" or not x_disp_q.is_contiguous():
+        raise ValueError("x_disp_q: expected a contiguous device tensor")
+    st = lib.moe_expert_ffn_fp8(ctypes.byref(cfg), int(capacity),
+                                ctypes.c_void_p(x_disp_q.data_ptr()),
+                                _ptr(scale, "f32", cfg, "scale"),
+                                _ptr(expert_offsets, "i32", cfg, "expert_offsets"),
+                                _ptr(w1, "act", cfg, "w1"), _ptr(b1, "f32", cfg, "b1"),
+                                _ptr(w2, "act", cfg, "w2"), _ptr(b2, "f32", cfg, "b2"),
+                                _ptr(h_buf, "act", cfg, "h_buf"), _ptr(y, "f32", cfg, "y"),
+                                int(bool(packed)), _stream(stream))
+    _check("moe_expert_ffn_fp8", st)
+
+
+def moe_expert_rank_affinity(cfg: MoeCfg, topk_idx, route_row, src_rank, n_ep: int, affinity,
+                             stream=None) -> None:
+    """affinity [E, n_ep] int32 (device): routes to expert e from source rank r
+    (accepted routes only when route_row is given)."""
+    lib = load_library()
+    st = lib.moe_expert_rank_affinity(ctypes.byref(cfg), _ptr(topk_idx, "i32", cfg, "topk_idx"),
+                                      _ptr(route_row, "i32", cfg, "route_row"),
+                                      _ptr(src_rank, "i32", cfg, "src_rank"), int(n_ep),
+                                      _ptr(affinity, "i32", cfg, "affinity"), _stream(stream))
+    _check("moe_expert_rank_affinity", st)
+
+
+def moe_place_experts(affinity, n_ep: int):
+    """Expert -> rank map (list of E ints) with E / n_ep experts per rank that
+    maximises the local routes (pure host call on a host copy of `affinity`)."""
+    lib = load_library()
+    a = torch.as_tensor(affinity).to("cpu", torch.int32).contiguous()
+    E = int(a.shape[0])
+    owner = (ctypes.c_int32 * E)()
+    st = lib.moe_place_experts(ctypes.c_void_p(a.data_ptr()), E, int(n_ep), owner)
+    _check("moe_place_experts", st)
+    return list(owner)

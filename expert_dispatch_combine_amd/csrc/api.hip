@@ -307,6 +307,28 @@ int moe_expert_ffn_rows(const moe_cfg* cfg, int64_t capacity, const void* x,
                            y, packed != 0, stream);
 }
 
+int moe_expert_ffn_fp8(const moe_cfg* cfg, int64_t capacity, const uint8_t* x_disp_q,
+                       const float* scale, const int32_t* expert_offsets, const void* w1,
+                       const float* b1, const void* w2, const float* b2, void* h_buf, float* y,
+                       int32_t packed, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (!ffn_fp8_supported(cfg->E, cfg->F, routes_of(cfg), capacity)) return MOE_ERR_UNSUPPORTED;
+  const int64_t rmax = rows_max(cfg, capacity);
+  if (rmax == 0) return MOE_OK;
+  if (!x_disp_q || !scale || !expert_offsets || !w1 || !b1 || !w2 || !b2 || !h_buf || !y)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_disp_q) || !aligned16(w1) || !aligned16(w2) || !aligned16(h_buf) ||
+      !aligned16(y) || !aligned16(b1) || !aligned16(b2))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_ffn_fp8(x_disp_q, scale, expert_offsets, (const uint16_t*)w1, b1,
+                                   (const uint16_t*)w2, b2, (uint16_t*)h_buf, y, cfg->E, cfg->h,
+                                   cfg->F, routes_of(cfg), capacity, rmax, packed != 0,
+                                   (hipStream_t)stream));
+}
+
 int moe_pack_expert_weights(const moe_cfg* cfg, const void* w1, const void* w2,
                             void* w1_packed, void* w2_packed, void* stream) {
   int st = check_cfg(cfg);

@@ -16,6 +16,13 @@
 
 namespace moe {
 
+
+// Expert outputs are read once: nontemporal loads.
+__device__ __forceinline__ float ntl(const float* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float4 ntl(const float4* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return __builtin_bit_cast(float4, v);
+}
 constexpr int kMaxTB = 64;  // tokens per combine workgroup
 // LDS of one combine workgroup: the tokens' rows and gates
 constexpr int kCombineLdsBytes = kMaxTB * kMaxTopK * 8;
@@ -45,8 +52,9 @@ inline CombineShape combine_shape(int T, int h) {
 }
 
 // Workgroup b's tokens [b TB, b TB + TB).  Each thread takes U output vectors
-// at a time and issues the U loads of one k before their FMAs, so it waits
-// on memory K times per U vectors.  s_row / s_gate: LDS of TB * K entries.
+// at a time; the U loads of route k + 1 are issued before the FMAs of route
+// k, so one route's rows are always in flight while the previous one is
+// added.  s_row / s_gate: LDS of TB * K entries.
 template <bool VEC, int U>
 __device__ __forceinline__ void combine_tokens(int b, const float* __restrict__ y,
                                                const int32_t* __restrict__ route_row,
@@ -78,21 +86,32 @@ __device__ __forceinline__ void combine_tokens(int b, const float* __restrict__ 
 #pragma unroll
       for (int q = 0; q < NV; ++q) acc[u][q] = 0.f;
     }
+    V v[U];
+    int r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      r[u] = s_row[tl[u] * K];
+      if (r[u] >= 0) v[u] = ntl(&yv[(size_t)r[u] * hv + c[u]]);
+    }
     for (int k = 0; k < K; ++k) {
-      V v[U];
-      int r[U];
+      V vn[U];
+      int rn[U];
+      const int kn = k + 1 < K ? k + 1 : k;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        r[u] = s_row[tl[u] * K + k];
-        if (r[u] >= 0) v[u] = yv[(size_t)r[u] * hv + c[u]];
+        rn[u] = k + 1 < K ? s_row[tl[u] * K + kn] : -1;
+        if (rn[u] >= 0) vn[u] = ntl(&yv[(size_t)rn[u] * hv + c[u]]);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (r[u] < 0) continue;
-        const float g = s_gate[tl[u] * K + k];
-        const float* vf = (const float*)&v[u];
+        if (r[u] >= 0) {
+          const float g = s_gate[tl[u] * K + k];
+          const float* vf = (const float*)&v[u];
 #pragma unroll
-        for (int q = 0; q < NV; ++q) acc[u][q] = fmaf(g, vf[q], acc[u][q]);
+          for (int q = 0; q < NV; ++q) acc[u][q] = fmaf(g, vf[q], acc[u][q]);
+        }
+        v[u] = vn[u];
+        r[u] = rn[u];
       }
     }
 #pragma unroll

@@ -25,6 +25,9 @@
 //  * streaming (rows per expert up to a few hundred: weight-bandwidth bound).
 //    A workgroup takes ALL rows of one expert (up to 160, in 32-row MFMA
 //    tiles) and 32*WN weight rows, so each weight byte crosses HBM once.
+//    Weights are read once, with nontemporal loads (streamed past the caches
+//    that keep the activations), and the fp32 outputs of the second GEMM are
+//    written with nontemporal stores.
 //    Weights go straight from global memory into a register ring PD chunks
 //    deep (no LDS); activations are shared by the 4 waves through a
 //    double-buffered, XOR-swizzled LDS tile, loaded two chunks ahead (four
@@ -49,6 +52,8 @@
 // capacity fits one row tile of the streaming shape, every expert has one row
 // tile whatever the routing, so the map needs no `offsets` and the weight
 // prefetch starts before the expert's row range is read.
+#include <type_traits>
+
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -82,6 +87,46 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
+
+// OCP E4M3 code -> fp32, exactly (finite codes: the quantiser never writes
+// the NaN code).  A normal code's 4-bit exponent (bias 7) and 3-bit mantissa
+// move into the fp32 fields (exponent + 120); exponent 0 is subnormal,
+// m * 2^-9.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t em = c & 0x7Fu;
+  const float mag = em < 8u ? (float)em * 0x1p-9f : __uint_as_float((em << 20) + (120u << 23));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// eight E4M3 codes (lo: codes 0-3, hi: 4-7) -> eight bf16 of value * scale,
+// the receiver's dequantisation of the FP8 payload: the product of a 4-bit
+// and an 8-bit significand is exact in fp32 and is rounded once to bf16.
+__device__ __forceinline__ u32x4 dequant8(uint32_t lo, uint32_t hi, float scale) {
+  u32x4 o;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t w = p < 2 ? lo : hi;
+    const int sh = 16 * (p & 1);
+    o[p] = pack_bf16x2(e4m3_to_f32((w >> sh) & 0xFFu) * scale,
+                       e4m3_to_f32((w >> (sh + 8)) & 0xFFu) * scale);
+  }
+  return o;
+}
+
+// Activation elements of the first GEMM: bf16 (AB = 2 bytes) or E4M3 codes
+// of the FP8 dispatch payload (AB = 1), widened to bf16 x scale when staged.
+template <int AB>
+struct ActIn {
+  using V = typename std::conditional<AB == 2, u32x4, uint2>::type;  // 8 elements
+  static __device__ __forceinline__ u32x4 widen(const V& v, float scale) {
+    if constexpr (AB == 2) {
+      (void)scale;
+      return v;
+    } else {
+      return dequant8(v.x, v.y, scale);
+    }
+  }
+};
 
 struct TileInfo {
   int e, row0, row_end, n0;
@@ -198,13 +243,17 @@ struct StreamShape {
 // range arrives, and a workgroup of an empty expert leaves after reading it.
 // rowmap != nullptr: activation row r is A[rowmap[r]] (the dispatch gather,
 // done by the loads themselves: A is then the token matrix x).
-template <int MT, int WN, int WK, int EPI, bool PK, int OCC>
+// AB: activation bytes per element, 2 (bf16) or 1 (E4M3 codes, widened to
+// bf16 x *ascale before they are staged in LDS).
+template <int MT, int WN, int WK, int EPI, bool PK, int OCC, int AB>
 __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+    const void* __restrict__ A, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, void* __restrict__ out,
     const int32_t* __restrict__ offsets, int E, int N, int Kd, int one_rt,
-    const int32_t* __restrict__ rowmap) {
+    const int32_t* __restrict__ rowmap, const float* __restrict__ ascale) {
   using S = StreamShape<MT, WN, WK, OCC>;
+  using AI = ActIn<AB>;
+  using AV = typename AI::V;
   static_assert(S::PD % S::AD == 0 && S::PD % 2 == 0, "ring sizes");
   // the epilogue stages all BM output rows at once when they fit in 48 KB
   constexpr int OUT_ALL = MT * 32 * (S::BN * (EPI == 0 ? 2 : 4) + 16);
@@ -249,7 +298,8 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
   for (int p = 0; p < S::PD - 1; ++p)
     if (p < nchunks)
 #pragma unroll
-      for (int q = 0; q < S::KSTEPS; ++q) wr[p][q] = *(const u32x4*)(wp + p * CSTR + q * QSTR);
+      for (int q = 0; q < S::KSTEPS; ++q)
+        wr[p][q] = __builtin_nontemporal_load((const u32x4*)(wp + p * CSTR + q * QSTR));
   if (one_rt) {
     row0 = offsets[e];
     row_end = offsets[e + 1];
@@ -257,16 +307,17 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
   }
 
   // ---- activations: this thread stages MT quads per chunk (row c/8, quad c%8)
-  const uint16_t* ap[MT];
+  const char* ap[MT];
   int alds[MT];
 #pragma unroll
   for (int j = 0; j < MT; ++j) {
     const int c = tid + 256 * j;
     const int r = c >> 3, q = c & 7;
     const int row = min(row0 + r, row_end - 1);
-    ap[j] = A + (size_t)(rowmap ? rowmap[row] : row) * Kd + q * 8;
+    ap[j] = (const char*)A + ((size_t)(rowmap ? rowmap[row] : row) * Kd + q * 8) * AB;
     alds[j] = act_slot(r, q);
   }
+  const float asc = AB == 1 ? *ascale : 0.0f;
   // activation fragments: the quad of the chunk that matches the weights' k
   int afrag[MT][S::KSTEPS];
 #pragma unroll
@@ -287,16 +338,16 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
 
   // activations: chunk 0 straight into LDS stage 0, chunks 1 .. AD-1 into
   // register slots; chunk c+AD is always in flight while chunk c is computed
-  u32x4 areg[S::AD][MT];
+  AV areg[S::AD][MT];
 #pragma unroll
-  for (int j = 0; j < MT; ++j) areg[0][j] = *(const u32x4*)(ap[j]);
+  for (int j = 0; j < MT; ++j) areg[0][j] = *(const AV*)(ap[j]);
 #pragma unroll
   for (int a = 1; a < S::AD; ++a)
     if (a < nchunks)
 #pragma unroll
-      for (int j = 0; j < MT; ++j) areg[a][j] = *(const u32x4*)(ap[j] + a * S::KC);
+      for (int j = 0; j < MT; ++j) areg[a][j] = *(const AV*)(ap[j] + a * S::KC * AB);
 #pragma unroll
-  for (int j = 0; j < MT; ++j) *(u32x4*)(act + alds[j]) = areg[0][j];
+  for (int j = 0; j < MT; ++j) *(u32x4*)(act + alds[j]) = AI::widen(areg[0][j], asc);
   __syncthreads();
 
   // One k-chunk c (PD is a multiple of AD and of 2, so every slot index is
@@ -313,12 +364,12 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     const uint16_t* stage_ = act + (STG) * S::STAGE;                                  \
     if (HAS_NEXTA) {                                                                  \
       _Pragma("unroll") for (int j = 0; j < MT; ++j) areg[ASLOT][j] =                 \
-          *(const u32x4*)(ap[j] + ((c) + S::AD) * S::KC);                             \
+          *(const AV*)(ap[j] + ((c) + S::AD) * S::KC * AB);                           \
     }                                                                                 \
     if (REFILL) {                                                                     \
       _Pragma("unroll") for (int q = 0; q < S::KSTEPS; ++q)                           \
         wr[((SLOT) + S::PD - 1) % S::PD][q] =                                         \
-            *(const u32x4*)(wp + ((c) + S::PD - 1) * CSTR + q * QSTR);                \
+            __builtin_nontemporal_load((const u32x4*)(wp + ((c) + S::PD - 1) * CSTR + q * QSTR)); \
     }                                                                                 \
     if constexpr (OCC == 1) {                                                         \
       /* one wave per SIMD: nothing else hides LDS latency, so every fragment */      \
@@ -347,7 +398,7 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     if (HAS_NEXT) {                                                                   \
       uint16_t* nst_ = act + ((STG) ^ 1) * S::STAGE;                                  \
       _Pragma("unroll") for (int j = 0; j < MT; ++j) *(u32x4*)(nst_ + alds[j]) =      \
-          areg[NSLOT][j];                                                             \
+          AI::widen(areg[NSLOT][j], asc);                                             \
     }                                                                                 \
     __syncthreads();                                                                  \
   } while (0)
@@ -431,7 +482,10 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     char* gout = (char*)out + ((size_t)row0 * N + n0) * ESZ;
     for (int i = tid; i < rows * CPR; i += 256) {
       const int r = i / CPR, c = i - r * CPR;
-      *(u32x4*)(gout + (size_t)r * N * ESZ + c * 16) = *(const u32x4*)(tile + r * ROWB + c * 16);
+      const u32x4 v = *(const u32x4*)(tile + r * ROWB + c * 16);
+      u32x4* dst = (u32x4*)(gout + (size_t)r * N * ESZ + c * 16);
+      if (EPI == 1) __builtin_nontemporal_store(v, dst);  // Y: read back only by the combine
+      else *dst = v;                                       // H: read next by the second GEMM
     }
     return;
   }
@@ -460,7 +514,10 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     char* gout = (char*)out + ((size_t)(row0 + tm * 32) * N + n0) * ESZ;
     for (int i = tid; i < rows * CPR; i += 256) {
       const int r = i / CPR, c = i - r * CPR;
-      *(u32x4*)(gout + (size_t)r * N * ESZ + c * 16) = *(const u32x4*)(tile + r * ROWB + c * 16);
+      const u32x4 v = *(const u32x4*)(tile + r * ROWB + c * 16);
+      u32x4* dst = (u32x4*)(gout + (size_t)r * N * ESZ + c * 16);
+      if (EPI == 1) __builtin_nontemporal_store(v, dst);  // Y: read back only by the combine
+      else *dst = v;                                       // H: read next by the second GEMM
     }
   }
 }
@@ -613,12 +670,14 @@ __global__ __launch_bounds__(256, 2) void tiled_gemm_kernel(
 // staging are spread over the four k-steps: issued in one burst they held
 // each chunk's first step up by several hundred ns.  256 x 256: one
 // workgroup per CU (the accumulators fill the AGPRs); 128 x 128: two.
-template <int WBM, int BN, int EPI, bool PK, int OCC>
+// AB: activation bytes per element, 2 (bf16) or 1 (E4M3 codes, widened to
+// bf16 x *ascale when staged; a code quad occupies the low half of its slot).
+template <int WBM, int BN, int EPI, bool PK, int OCC, int AB>
 __global__ __launch_bounds__(256, OCC) void wide_gemm_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+    const void* __restrict__ A, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, void* __restrict__ out,
     const int32_t* __restrict__ offsets, int E, int N, int Kd,
-    const int32_t* __restrict__ rowmap) {
+    const int32_t* __restrict__ rowmap, const float* __restrict__ ascale) {
   constexpr int TM = WBM / 64;         // 32-row MFMA tiles per wave
   constexpr int TN = BN / 64;          // 32-column MFMA tiles per wave
   constexpr int AQ = WBM * 8 / 256;    // 16-byte quads per thread and chunk: activations
@@ -644,7 +703,9 @@ __global__ __launch_bounds__(256, OCC) void wide_gemm_kernel(
   // swizzle of row r + 32 j equals that of r, so LDS slots step by 32 rows.
   // rowmap: the base is the token matrix and the offsets name token rows (the
   // host keeps its element count below 2^32)
-  const uint16_t* abase = rowmap ? A : A + (size_t)row0 * Kd;
+  const uint16_t* abase = (const uint16_t*)A + (rowmap ? 0 : (size_t)row0 * Kd);
+  const uint8_t* abase8 = (const uint8_t*)A + (rowmap ? 0 : (size_t)row0 * Kd);
+  const float asc = AB == 1 ? *ascale : 0.0f;
   const uint16_t* wbase = PK ? W + ((size_t)e * (N / 32) + n0 / 32) * nk * PBLK
                              : W + ((size_t)e * N + n0) * Kd;
   const int sr = tid >> 3, sq = tid & 7;
@@ -684,12 +745,32 @@ __global__ __launch_bounds__(256, OCC) void wide_gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
 
+  // activation quad at element offset `o`: 8 bf16, or 8 E4M3 codes in the
+  // low half of the slot (widened when staged)
+  auto load_act = [](const uint16_t* b16, const uint8_t* b8, uint32_t o) -> u32x4 {
+    if constexpr (AB == 2) {
+      (void)b8;
+      return *(const u32x4*)(b16 + o);
+    } else {
+      (void)b16;
+      const uint2 v = *(const uint2*)(b8 + o);
+      return u32x4{v.x, v.y, 0u, 0u};
+    }
+  };
+  auto widen_act = [](const u32x4& v, float scale) -> u32x4 {
+    if constexpr (AB == 2) {
+      (void)scale;
+      return v;
+    } else {
+      return dequant8(v[0], v[1], scale);
+    }
+  };
   // global -> registers two chunks ahead; LDS fragments one k-step ahead
   u32x4 reg[2][NQ];
 #define MOE_WIDE_LOAD(SLOT, c)                                                               \
   do {                                                                                       \
     _Pragma("unroll") for (int j = 0; j < AQ; ++j) reg[SLOT][j] =                            \
-        *(const u32x4*)(abase + (aoff[j] + (uint32_t)(c) * 64u));                            \
+        load_act(abase, abase8, aoff[j] + (uint32_t)(c) * 64u);                              \
     _Pragma("unroll") for (int j = 0; j < WQ; ++j) reg[SLOT][AQ + j] =                       \
         *(const u32x4*)(wbase + (woff0 + j * wjstr + (uint32_t)(c) * WCSTR));                \
   } while (0)
@@ -697,7 +778,7 @@ __global__ __launch_bounds__(256, OCC) void wide_gemm_kernel(
   do {                                                                                       \
     uint16_t* st_ = lds + (SLOT) * STG;                                                      \
     _Pragma("unroll") for (int j = 0; j < AQ; ++j) *(u32x4*)(st_ + adst + j * 32 * 64) =     \
-        reg[SLOT][j];                                                                        \
+        widen_act(reg[SLOT][j], asc);                                                        \
     _Pragma("unroll") for (int j = 0; j < WQ; ++j) *(u32x4*)(st_ + wdst + j * WDJ) =         \
         reg[SLOT][AQ + j];                                                                   \
   } while (0)
@@ -727,7 +808,7 @@ __global__ __launch_bounds__(256, OCC) void wide_gemm_kernel(
         _Pragma("unroll") for (int jj = 0; jj < QPS; ++jj) {                                 \
           const int j = s4 * QPS + jj;                                                       \
           if (j < AQ)                                                                        \
-            reg[SLOT][j] = *(const u32x4*)(abase + (aoff[j] + (uint32_t)((c) + 2) * 64u));   \
+            reg[SLOT][j] = load_act(abase, abase8, aoff[j] + (uint32_t)((c) + 2) * 64u);     \
           else                                                                               \
             reg[SLOT][j] = *(const u32x4*)(wbase + (woff0 + (j - AQ) * wjstr +               \
                                                     (uint32_t)((c) + 2) * WCSTR));           \
@@ -743,7 +824,7 @@ __global__ __launch_bounds__(256, OCC) void wide_gemm_kernel(
         _Pragma("unroll") for (int jj = 0; jj < QPS; ++jj) {                                 \
           const int j = s4 * QPS + jj;                                                       \
           if (j < AQ)                                                                        \
-            *(u32x4*)(nst + adst + j * 32 * 64) = reg[(SLOT) ^ 1][j];                        \
+            *(u32x4*)(nst + adst + j * 32 * 64) = widen_act(reg[(SLOT) ^ 1][j], asc);        \
           else                                                                               \
             *(u32x4*)(nst + wdst + (j - AQ) * WDJ) = reg[(SLOT) ^ 1][j];                     \
         }                                                                                    \
@@ -858,68 +939,66 @@ int64_t grid_for(int64_t r_max, int BM, int E, int N, int BN) {
   return (g + NXCD - 1) / NXCD * NXCD;
 }
 
-template <int MT, int WN, int WK, int EPI, bool PK, int OCC>
-hipError_t launch_stream(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
-                         const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
-                         bool static_map, const int32_t* rowmap, hipStream_t s) {
+// Launch arguments shared by every GEMM shape.  A: activations (bf16, or
+// E4M3 codes when the launcher's AB is 1, scaled by *ascale); rowmap: row r
+// of the tile reads A[rowmap[r]] (the gather of the dispatch), or nullptr.
+struct GemmArgs {
+  const void* A;
+  const uint16_t* W;
+  const float* bias;
+  void* out;
+  const int32_t* offsets;
+  int E, N, Kd;
+  int64_t r_max;
+  const int32_t* rowmap;
+  const float* ascale;
+  hipStream_t s;
+};
+
+template <int MT, int WN, int WK, int EPI, bool PK, int OCC, int AB>
+hipError_t launch_stream(const GemmArgs& g, bool static_map) {
   // static_map: every expert's rows fit one row tile (see the kernel)
   const int one_rt = static_map ? 1 : 0;
-  const int64_t grid = one_rt ? ((int64_t)E * (N / (32 * WN)) + NXCD - 1) / NXCD * NXCD
-                              : grid_for(r_max, 32 * MT, E, N, 32 * WN);
-  hipLaunchKernelGGL((stream_gemm_kernel<MT, WN, WK, EPI, PK, OCC>), dim3((unsigned)grid),
-                     dim3(256), 0, s, A, W, bias, out, offsets, E, N, Kd, one_rt, rowmap);
+  const int64_t grid = one_rt ? ((int64_t)g.E * (g.N / (32 * WN)) + NXCD - 1) / NXCD * NXCD
+                              : grid_for(g.r_max, 32 * MT, g.E, g.N, 32 * WN);
+  hipLaunchKernelGGL((stream_gemm_kernel<MT, WN, WK, EPI, PK, OCC, AB>), dim3((unsigned)grid),
+                     dim3(256), 0, g.s, g.A, g.W, g.bias, g.out, g.offsets, g.E, g.N, g.Kd, one_rt,
+                     g.rowmap, g.ascale);
   return hipGetLastError();
 }
 
-template <int MT, int WN, int WK, int EPI, bool PK>
-hipError_t launch_stream_occ(bool occ1, const uint16_t* A, const uint16_t* W, const float* bias,
-                             void* out, const int32_t* offsets, int E, int N, int Kd,
-                             int64_t r_max, bool static_map, const int32_t* rowmap,
-                             hipStream_t s) {
+template <int MT, int WN, int WK, int EPI, bool PK, int AB>
+hipError_t launch_stream_occ(const GemmArgs& g, bool occ1, bool static_map) {
   // built only for the tall tiles, where one workgroup per CU is the common case
   if constexpr (MT >= 4 && WN == 2)
-    if (occ1)
-      return launch_stream<MT, WN, WK, EPI, PK, 1>(A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                   static_map, rowmap, s);
-  return launch_stream<MT, WN, WK, EPI, PK, 2>(A, W, bias, out, offsets, E, N, Kd, r_max,
-                                               static_map, rowmap, s);
+    if (occ1) return launch_stream<MT, WN, WK, EPI, PK, 1, AB>(g, static_map);
+  return launch_stream<MT, WN, WK, EPI, PK, 2, AB>(g, static_map);
 }
 
-template <int MT, int EPI, bool PK>
-hipError_t launch_stream_mt(int wn, bool occ1, const uint16_t* A, const uint16_t* W,
-                            const float* bias, void* out, const int32_t* offsets, int E, int N,
-                            int Kd, int64_t r_max, bool static_map, const int32_t* rowmap,
-                            hipStream_t s) {
-  if (wn == 4)
-    return launch_stream_occ<MT, 4, 1, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                static_map, rowmap, s);
+template <int MT, int EPI, bool PK, int AB>
+hipError_t launch_stream_mt(const GemmArgs& g, int wn, bool occ1, bool static_map) {
+  if (wn == 4) return launch_stream_occ<MT, 4, 1, EPI, PK, AB>(g, occ1, static_map);
   // the 4-way k split keeps MT <= 3 (its reduction and ring outgrow the registers)
-  if (wn == 2 || MT >= 4)
-    return launch_stream_occ<MT, 2, 2, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                static_map, rowmap, s);
-  if constexpr (MT < 4)
-    return launch_stream_occ<MT, 1, 4, EPI, PK>(occ1, A, W, bias, out, offsets, E, N, Kd, r_max,
-                                                static_map, rowmap, s);
+  if (wn == 2 || MT >= 4) return launch_stream_occ<MT, 2, 2, EPI, PK, AB>(g, occ1, static_map);
+  if constexpr (MT < 4) return launch_stream_occ<MT, 1, 4, EPI, PK, AB>(g, occ1, static_map);
   return hipErrorInvalidValue;
 }
 
-template <int WBM, int BN, int EPI, bool PK, int OCC>
-hipError_t launch_wide(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
-                       const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
-                       const int32_t* rowmap, hipStream_t s) {
-  const int64_t grid = grid_for(r_max, WBM, E, N, BN);
-  hipLaunchKernelGGL((wide_gemm_kernel<WBM, BN, EPI, PK, OCC>), dim3((unsigned)grid), dim3(256),
-                     0, s, A, W, bias, out, offsets, E, N, Kd, rowmap);
+template <int WBM, int BN, int EPI, bool PK, int OCC, int AB>
+hipError_t launch_wide(const GemmArgs& g) {
+  const int64_t grid = grid_for(g.r_max, WBM, g.E, g.N, BN);
+  hipLaunchKernelGGL((wide_gemm_kernel<WBM, BN, EPI, PK, OCC, AB>), dim3((unsigned)grid),
+                     dim3(256), 0, g.s, g.A, g.W, g.bias, g.out, g.offsets, g.E, g.N, g.Kd,
+                     g.rowmap, g.ascale);
   return hipGetLastError();
 }
 
 template <int BN, int EPI, bool PK>
-hipError_t launch_tiled(const uint16_t* A, const uint16_t* W, const float* bias, void* out,
-                        const int32_t* offsets, int E, int N, int Kd, int64_t r_max,
-                        const int32_t* rowmap, hipStream_t s) {
-  const int64_t grid = grid_for(r_max, TBM, E, N, BN);
-  hipLaunchKernelGGL((tiled_gemm_kernel<BN, EPI, PK>), dim3((unsigned)grid), dim3(256), 0, s,
-                     A, W, bias, out, offsets, E, N, Kd, rowmap);
+hipError_t launch_tiled(const GemmArgs& g) {
+  const int64_t grid = grid_for(g.r_max, TBM, g.E, g.N, BN);
+  hipLaunchKernelGGL((tiled_gemm_kernel<BN, EPI, PK>), dim3((unsigned)grid), dim3(256), 0, g.s,
+                     (const uint16_t*)g.A, g.W, g.bias, g.out, g.offsets, g.E, g.N, g.Kd,
+                     g.rowmap);
   return hipGetLastError();
 }
 
@@ -941,20 +1020,21 @@ bool takes_wide_shape(bool first, int N, int64_t rows_typ) {
   return (rows_typ >= 512 && N % 256 == 0 && first) || (rows_typ >= 384 && N % 128 == 0);
 }
 
-template <int EPI, bool PK>
-hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* bias,
-                            void* out, const int32_t* offsets, int E, int N, int Kd,
-                            int64_t r_max, int64_t rows_typ, int64_t rows_max,
-                            const int32_t* rowmap, hipStream_t s) {
+// Whether the tiled shape serves this GEMM (it reads bf16 activations only).
+bool takes_tiled_shape(int N, int64_t rows_typ) {
+  return rows_typ >= 384 && N % 128 != 0;
+}
+
+template <int EPI, bool PK, int AB>
+hipError_t launch_gemm_auto(const GemmArgs& g, int64_t rows_typ, int64_t rows_max) {
+  const int E = g.E, N = g.N;
   if constexpr (EPI == 0)  // the 256 x 256 tiles serve the first GEMM only
-    if (rows_typ >= 512 && N % 256 == 0)
-      return launch_wide<256, 256, EPI, PK, 1>(A, W, bias, out, offsets, E, N, Kd, r_max,
-                                               rowmap, s);
-  if (rows_typ >= 384 && N % 128 == 0)
-    return launch_wide<128, 128, EPI, PK, 2>(A, W, bias, out, offsets, E, N, Kd, r_max, rowmap,
-                                             s);
-  if (rows_typ >= 384)
-    return launch_tiled<64, EPI, PK>(A, W, bias, out, offsets, E, N, Kd, r_max, rowmap, s);
+    if (rows_typ >= 512 && N % 256 == 0) return launch_wide<256, 256, EPI, PK, 1, AB>(g);
+  if (rows_typ >= 384 && N % 128 == 0) return launch_wide<128, 128, EPI, PK, 2, AB>(g);
+  if (rows_typ >= 384) {
+    if constexpr (AB == 2) return launch_tiled<64, EPI, PK>(g);
+    return hipErrorNotSupported;
+  }
   int mt = (int)((rows_max + 31) / 32);
   if (mt > 5) mt = 4;
   if (mt < 1) mt = 1;
@@ -963,22 +1043,18 @@ hipError_t launch_gemm_auto(const uint16_t* A, const uint16_t* W, const float* b
   // workgroups would prefetch weights for nothing.
   const bool one_rt = rows_max <= 32 * mt && 2 * rows_typ >= 32 * mt;
   const int64_t bm = 32 * mt;
-  const int64_t mtiles = (r_max + bm - 1) / bm > E ? (r_max + bm - 1) / bm : E;
+  const int64_t mtiles = (g.r_max + bm - 1) / bm > E ? (g.r_max + bm - 1) / bm : E;
   int wn = 1;
   if (N % 128 == 0 && mtiles * (N / 128) >= 256) wn = 4;
   else if (mtiles * (N / 64) >= 256 || mt >= 4) wn = 2;
   // at most one workgroup of work per CU: build for occupancy 1 and prefetch deeper
   const bool occ1 = mtiles * (N / (32 * wn)) <= 256;
   switch (mt) {
-#define MOE_MT_CASE(M_)                                                                    \
-    return launch_stream_mt<M_, EPI, PK>(wn, occ1, A, W, bias, out, offsets, E, N, Kd, r_max, \
-                                         one_rt, rowmap, s)
-    case 1: MOE_MT_CASE(1);
-    case 2: MOE_MT_CASE(2);
-    case 3: MOE_MT_CASE(3);
-    case 4: MOE_MT_CASE(4);
-    default: MOE_MT_CASE(5);
-#undef MOE_MT_CASE
+    case 1: return launch_stream_mt<1, EPI, PK, AB>(g, wn, occ1, one_rt);
+    case 2: return launch_stream_mt<2, EPI, PK, AB>(g, wn, occ1, one_rt);
+    case 3: return launch_stream_mt<3, EPI, PK, AB>(g, wn, occ1, one_rt);
+    case 4: return launch_stream_mt<4, EPI, PK, AB>(g, wn, occ1, one_rt);
+    default: return launch_stream_mt<5, EPI, PK, AB>(g, wn, occ1, one_rt);
   }
 }
 
@@ -1004,11 +1080,31 @@ hipError_t launch_ffn_bf16_t(const uint16_t* xd, const int32_t* row_token, int64
     xd = (const uint16_t*)y;
     row_token = nullptr;
   }
-  hipError_t err = launch_gemm_auto<0, PK>(xd, w1, b1, hbuf, offsets, E, F, h, r_max, rows_typ,
-                                           rows_max, row_token, s);
+  hipError_t err = launch_gemm_auto<0, PK, 2>(
+      {xd, w1, b1, hbuf, offsets, E, F, h, r_max, row_token, nullptr, s}, rows_typ, rows_max);
   if (err != hipSuccess) return err;
-  return launch_gemm_auto<1, PK>(hbuf, w2, b2, y, offsets, E, h, F, r_max, rows_typ, rows_max,
-                                 nullptr, s);
+  return launch_gemm_auto<1, PK, 2>({hbuf, w2, b2, y, offsets, E, h, F, r_max, nullptr, nullptr, s},
+                                    rows_typ, rows_max);
+}
+
+// The expert FFN on the FP8 dispatch payload: GEMM1 reads the E4M3 codes of
+// the dispatched rows and widens them to bf16 x scale as it stages them;
+// GEMM2 is the bf16 one.  hipErrorNotSupported where GEMM1 would take the
+// tiled shape.
+template <bool PK>
+hipError_t launch_ffn_fp8_t(const uint8_t* xq, const float* scale, const int32_t* offsets,
+                            const uint16_t* w1, const float* b1, const uint16_t* w2,
+                            const float* b2, uint16_t* hbuf, float* y, int E, int h, int F,
+                            int64_t A, int64_t cap, int64_t r_max, hipStream_t s) {
+  if (r_max == 0) return hipSuccess;
+  const int64_t avg = (A + E - 1) / E;
+  const int64_t rows_typ = avg < cap ? avg : cap;
+  const int64_t rows_max = A < cap ? A : cap;
+  hipError_t err = launch_gemm_auto<0, PK, 1>(
+      {xq, w1, b1, hbuf, offsets, E, F, h, r_max, nullptr, scale, s}, rows_typ, rows_max);
+  if (err != hipSuccess) return err;
+  return launch_gemm_auto<1, PK, 2>({hbuf, w2, b2, y, offsets, E, h, F, r_max, nullptr, nullptr, s},
+                                    rows_typ, rows_max);
 }
 
 }  // namespace
@@ -1023,6 +1119,22 @@ hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* row_token, int64_t
                                    h, F, A, cap, r_max, s);
   return launch_ffn_bf16_t<false>(xd, row_token, x_rows, offsets, w1, b1, w2, b2, hbuf, y, E, h,
                                   F, A, cap, r_max, s);
+}
+
+bool ffn_fp8_supported(int E, int F, int64_t A, int64_t cap) {
+  const int64_t avg = E > 0 ? (A + E - 1) / E : 0;
+  return !takes_tiled_shape(F, avg < cap ? avg : cap);
+}
+
+hipError_t launch_ffn_fp8(const uint8_t* xq, const float* scale, const int32_t* offsets,
+                          const uint16_t* w1, const float* b1, const uint16_t* w2,
+                          const float* b2, uint16_t* hbuf, float* y, int E, int h, int F,
+                          int64_t A, int64_t cap, int64_t r_max, bool packed, hipStream_t s) {
+  if (packed)
+    return launch_ffn_fp8_t<true>(xq, scale, offsets, w1, b1, w2, b2, hbuf, y, E, h, F, A, cap,
+                                  r_max, s);
+  return launch_ffn_fp8_t<false>(xq, scale, offsets, w1, b1, w2, b2, hbuf, y, E, h, F, A, cap,
+                                 r_max, s);
 }
 
 hipError_t launch_pack_weights(const uint16_t* w, uint16_t* wp, int E, int N, int Kd,

@@ -162,6 +162,21 @@ int moe_fp8_dequantize(const moe_cfg* cfg, int64_t capacity, const uint8_t* x_di
                        const float* scale, const int32_t* expert_offsets, void* x_disp,
                        void* stream);
 
+/* The expert FFN on the FP8 dispatch payload ([DSV3] 4.3: the receiver
+ * dequantises the E4M3 hidden states before its experts): the H and Y of
+ * moe_expert_ffn (packed == 0) or moe_expert_ffn_packed (packed != 0) on
+ * x_disp[r] = bf16(value(x_disp_q[r]) * scale), with that dequantisation done
+ * by the first GEMM as it stages its activations (no bf16 copy of the rows
+ * is written).  x_disp_q [R_max, h] uint8 from moe_dispatch_fp8, scale the
+ * device fp32 from moe_fp8_scale; the other arguments as for moe_expert_ffn.
+ * bf16 only; MOE_ERR_UNSUPPORTED also where the first GEMM's rows per
+ * expert (min(capacity, ceil(T*K/E))) reach 384 while F is not a multiple of
+ * 128 (a shape whose kernel reads bf16 activations only). */
+int moe_expert_ffn_fp8(const moe_cfg* cfg, int64_t capacity, const uint8_t* x_disp_q,
+                       const float* scale, const int32_t* expert_offsets, const void* w1,
+                       const float* b1, const void* w2, const float* b2, void* h_buf, float* y,
+                       int32_t packed, void* stream);
+
 /* Aux-loss-free balancing: one step of the expert-bias rule of [DSV3]
  * section 八 (DeepSeekV3Gate), bias += alpha * (mean_count - count), where
  * count[e] = tokens whose largest bias-adjusted logit is expert e.
@@ -364,6 +379,28 @@ int moe_combine_ledger(const moe_cfg* cfg, const float* y, const int32_t* route_
 enum { MOE_PLAN_ACCEPT = 0, MOE_PLAN_TUNE = 1, MOE_PLAN_REJECT = 2 };
 int moe_recommend_plan(const moe_ledger_t* ledger, const double* thresholds,
                        int32_t use_locality);
+
+/* Locality-aware expert placement ([EP46] Step 3: a more local placement of
+ * the experts cuts cross-rank dispatch, watching whether the per-rank load
+ * gets skewed; [DSV3] 2.2: uniform placement of E / N experts per device,
+ * topology-aware placement matched on an affinity matrix by the Hungarian
+ * algorithm).
+ *
+ * moe_expert_rank_affinity: affinity [E, n_ep] int32 (device) = routes to
+ *   expert e from tokens of source rank r, over all routes (route_row NULL)
+ *   or over the accepted ones (route_row[t,k] >= 0).  Ids outside [0, E) and
+ *   ranks outside [0, n_ep) are not counted (moe_ledger reports them).
+ *   Asynchronous on `stream`; the matrix is cleared by the call itself.
+ * moe_place_experts: pure host function.  owner [E] int32 = the expert ->
+ *   rank map with E / n_ep experts per rank that maximises the routes kept
+ *   local, sum_e affinity[e][owner[e]] (affinity: host [E, n_ep] int32,
+ *   non-negative).  An exact assignment (O(E^3) integer Hungarian method);
+ *   when several maps reach the maximum, one of them.  E must be a multiple
+ *   of n_ep (else MOE_ERR_INVALID_ARG). */
+int moe_expert_rank_affinity(const moe_cfg* cfg, const int32_t* topk_idx,
+                             const int32_t* route_row, const int32_t* src_rank, int32_t n_ep,
+                             int32_t* affinity, void* stream);
+int moe_place_experts(const int32_t* affinity, int32_t E, int32_t n_ep, int32_t* owner);
 
 #ifdef __cplusplus
 }

@@ -9,8 +9,9 @@ import torch
 import expert_dispatch_combine_amd as M
 import moe_workloads as W
 import oracle as O
-from expert_dispatch_combine_amd.runner import LayerBuffers, run_combine, run_ffn
-from gpu_util import banner, bias_np, custom_inputs, device_inputs, host, oracle_logits, rms
+from expert_dispatch_combine_amd.runner import LayerBuffers, pack_weights, run_combine, run_ffn
+from gpu_util import (banner, bias_np, check_ffn_segment, custom_inputs, device_inputs, host,
+                      host_expert, oracle_logits, rms)
 
 pytestmark = pytest.mark.gpu
 
@@ -173,3 +174,92 @@ def test_fp8_layer_end_to_end():
     _, Y16 = O.expert_ffn(xd16, sl["expert_offsets"], host(inp.w1), host(inp.b1), host(inp.w2),
                           host(inp.b2), "bf16")
     assert rms(want - O.combine(Y16, sl["route_row"], gate)) <= 0.1 * rms(want)
+
+
+@pytest.mark.parametrize("cid,shape,packed", [
+    (2, None, True), (2, None, False),                 # streaming, one row tile per expert
+    (4, None, True),                                   # streaming, 128-row tiles, 256 experts
+    (5, None, True), (5, None, False),                 # wide 128 x 128 (hot experts)
+    (None, (4096, 256, 4, 1, 512, 1.0), True),         # wide 256 x 256 first GEMM
+    (None, (1000, 256, 4, 1, 320, 1.0), False),        # streaming with the tile search
+    (None, (513, 64, 64, 6, 128, 1.0), True)])         # many small / empty experts
+def test_fp8_ffn_equals_ffn_on_dequantised_rows(cid, shape, packed):
+    """moe_expert_ffn_fp8 (the first GEMM widens the E4M3 codes itself)
+    gives the same H and Y, bit for bit, as moe_expert_ffn(_packed) on the
+    rows moe_fp8_dequantize writes."""
+    banner(f"fp8 ffn cid={cid} shape={shape} packed={packed}")
+    if cid is not None:
+        inp = device_inputs(cid)
+    else:
+        T, h, E, K, F, cf = shape
+        inp = custom_inputs(W.custom(T=T, h=h, E=E, K=K, F=F, cf=cf, dtype="bf16",
+                                     seed=T * 5 + F))
+    cfg = inp.cfg
+    idx, _ = O.topk_softmax(oracle_logits(inp), cfg.K, bias_np(inp))
+    cap = O.capacity(cfg.T * cfg.K, cfg.E, cfg.cf)
+    mc, b, scale, scale_v, xq = _fp8_dispatch(inp, idx.astype(np.int32), cap)
+    R = int(b.expert_offsets[-1].item())
+    M.moe_fp8_dequantize(mc, cap, xq, scale, b.expert_offsets, b.x_disp)
+    w1, w2 = (pack_weights(mc, inp.w1, inp.w2) if packed else (inp.w1, inp.w2))
+    fn = M.moe_expert_ffn_packed if packed else M.moe_expert_ffn
+    fn(mc, cap, b.x_disp, b.expert_offsets, w1, inp.b1, w2, inp.b2, b.h_buf, b.y)
+    torch.cuda.synchronize()
+    h_ref, y_ref = b.h_buf[:R].clone(), b.y[:R].clone()
+    b.h_buf.fill_(7.0)
+    b.y.fill_(float("nan"))
+    M.moe_expert_ffn_fp8(mc, cap, xq, scale, b.expert_offsets, w1, inp.b1, w2, inp.b2, b.h_buf,
+                         b.y, packed)
+    torch.cuda.synchronize()
+    assert torch.equal(b.h_buf[:R], h_ref)
+    assert torch.equal(b.y[:R], y_ref)
+
+
+@pytest.mark.parametrize("cid", [2, 5])
+def test_fp8_step_end_to_end(cid):
+    """The FP8-payload step on the GPU: moe_route (router product), the
+    scale, the quantising dispatch, moe_expert_ffn_fp8 (packed weights) and
+    the combine, against the oracle fed the same routing (the GPU's ids and
+    gates: their own parity is checked elsewhere): every accepted row's H and
+    Y against O.expert_ffn_segment on the dequantised rows, and every token's
+    output within 2e-2 RMS of the oracle's combine."""
+    banner(f"fp8 step config {cid}")
+    inp = device_inputs(cid)
+    cfg = inp.cfg
+    mc = _mc(cfg)
+    cap = O.capacity(cfg.T * cfg.K, cfg.E, cfg.cf)
+    b = LayerBuffers(mc, cap)
+    M.moe_route(mc, inp.x, inp.w_gate, inp.logit_bias, b.logits, b.topk_idx, b.topk_gate, None,
+                b.ws)
+    scale = torch.zeros((1,), dtype=torch.float32, device="cuda")
+    M.moe_fp8_scale(mc, inp.x, scale, b.ws)
+    xq = torch.empty((max(b.r_max, 1), cfg.h), dtype=torch.uint8, device="cuda")
+    M.moe_dispatch_fp8(mc, inp.x, scale, b.topk_idx, cap, b.expert_offsets, b.route_rank,
+                       b.route_row, b.row_token, xq, None, b.ws)
+    w1, w2 = pack_weights(mc, inp.w1, inp.w2)
+    M.moe_expert_ffn_fp8(mc, cap, xq, scale, b.expert_offsets, w1, inp.b1, w2, inp.b2, b.h_buf,
+                         b.y, True)
+    run_combine(b)
+    torch.cuda.synchronize()
+    del w1, w2
+    scale_v = float(scale.item())
+    x64 = host(inp.x)
+    assert scale_v == O.fp8_scale(x64)
+    idx = b.topk_idx.cpu().numpy()
+    gate = b.topk_gate.cpu().numpy()
+    sl = O.slot_routes(idx, cfg.E, cap)
+    assert np.array_equal(b.route_row.cpu().numpy(), sl["route_row"])
+    R = sl["R"]
+    xd = O.fp8_dequantize(O.fp8_quantize(x64[sl["row_token"]], scale_v), scale_v)
+    H_g = b.h_buf[:R].float().cpu().numpy().astype(np.float64)
+    Y_g = b.y[:R].cpu().numpy().astype(np.float64)
+    offs = sl["expert_offsets"]
+    Y_o = np.zeros((R, cfg.h))
+    for e in range(cfg.E):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi > lo:
+            Y_o[lo:hi] = check_ffn_segment("bf16", xd[lo:hi], host_expert(inp.w1, e),
+                                           host_expert(inp.b1, e), host_expert(inp.w2, e),
+                                           host_expert(inp.b2, e), H_g[lo:hi], Y_g[lo:hi])
+    want = O.combine(Y_o, sl["route_row"], gate)
+    got = b.out.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - want)) <= 2e-2 * rms(want)

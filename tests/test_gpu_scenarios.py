@@ -15,7 +15,7 @@ import moe_workloads as W
 import oracle as O
 from expert_dispatch_combine_amd.runner import (LayerBuffers, capacity_of, cfg_from,
                                                 run_combine, run_dispatch, run_ffn, run_ledger)
-from gpu_util import banner, host, rms
+from gpu_util import banner, compare_ledger, host, rms
 
 pytestmark = pytest.mark.gpu
 
@@ -105,3 +105,81 @@ def test_plan_decision_at_the_3_decimal_boundary(loads, cf, want):
         assert led[k] == oled[k], k
     assert led["balance_ratio"] == oled["balance_ratio"]
     assert M.moe_recommend_plan(led) == O.recommend_plan(oled, oled) == want
+
+
+def _placement_case(mc, b, src_rank, n_ep, h, bytes_per_elem):
+    """Affinity on the GPU (bit-exact vs the oracle), the host placement (the
+    oracle's optimum of local routes, E / n_ep experts per rank), and the
+    GPU ledger under that placement against the oracle's ledger of the same
+    map.  Returns (round-robin ledger, placed ledger, owner)."""
+    E = mc.E
+    aff = torch.empty((E, n_ep), dtype=torch.int32, device="cuda")
+    M.moe_expert_rank_affinity(mc, b.topk_idx, None, src_rank, n_ep, aff)
+    torch.cuda.synchronize()
+    idx = b.topk_idx.cpu().numpy()
+    src = src_rank.cpu().numpy()
+    want = O.expert_rank_affinity(idx, src, E, n_ep)
+    aff_h = aff.cpu().numpy()
+    assert np.array_equal(aff_h, want)
+    row = b.route_row.cpu().numpy()
+    aff_acc = torch.empty_like(aff)
+    M.moe_expert_rank_affinity(mc, b.topk_idx, b.route_row, src_rank, n_ep, aff_acc)
+    torch.cuda.synchronize()
+    assert np.array_equal(aff_acc.cpu().numpy(),
+                          O.expert_rank_affinity(idx, src, E, n_ep, route_row=row))
+    owner = np.asarray(M.moe_place_experts(aff_h, n_ep), np.int32)
+    assert sorted(np.bincount(owner, minlength=n_ep).tolist()) == [E // n_ep] * n_ep
+    best = O.local_routes_under(want, O.locality_placement(want, n_ep))
+    assert O.local_routes_under(want, owner) == best
+    rr = np.arange(E, dtype=np.int32) % n_ep
+    gate = b.topk_gate.cpu().numpy()
+    leds = []
+    for own in (rr, owner):
+        g = run_ledger(b, src_rank, torch.from_numpy(own).cuda(), n_ep)
+        o = O.ledger(idx, gate, row, b.capacity, src, own, n_ep, hidden_size=h,
+                     bytes_per_elem=bytes_per_elem)
+        compare_ledger(g, o)
+        loads = O.rank_loads(idx, row, own, n_ep)
+        assert np.array_equal(np.asarray(g["pair_routes"]).sum(axis=0), loads)
+        assert M.moe_recommend_plan(g) == O.recommend_plan(o, o)
+        leds.append(g)
+    assert leds[1]["local_routes"] == best >= leds[0]["local_routes"]
+    return leds[0], leds[1], owner
+
+
+@pytest.mark.parametrize("name", W.ROUTING_SCENARIOS)
+def test_locality_placement_on_routing_scenario(name):
+    """[EP46] Step 3 (a more local expert placement) on the three routings
+    of its Step 5 workload: affinity, placement and the ledgers before and
+    after, against the oracle.  Local-heavy routing already favours the
+    round-robin owners, so the placement keeps its local routes; balanced
+    routing gains a little; the placement never loses local routes."""
+    banner(f"locality placement {name}")
+    cfg = W.SCENARIO_CONFIG
+    inp = _inputs()
+    mc = cfg_from(cfg)
+    b = LayerBuffers(mc, capacity_of(mc))
+    b.logits.copy_(torch.from_numpy(W.scenario_logits(name)))
+    M.moe_route(mc, None, None, None, b.logits, b.topk_idx, b.topk_gate, None, b.ws)
+    run_dispatch(b, inp.x, expert_load=True)
+    before, after, owner = _placement_case(mc, b, inp.src_rank, cfg.n_ep, cfg.h, 2)
+    if name == "local_heavy":
+        assert after["local_routes"] == before["local_routes"]
+    print(f"[placement] {name}: local hit {before['local_hit_ratio']:.4f} -> "
+          f"{after['local_hit_ratio']:.4f}, owner {owner.tolist()}", flush=True)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_locality_placement_on_workloads(cid):
+    """The same on the five workloads' own routing (GPU router)."""
+    banner(f"locality placement config {cid}")
+    from gpu_util import buffers_for, device_inputs
+    inp = device_inputs(cid, with_experts=cid in (3, 4))
+    cfg = inp.cfg
+    mc = cfg_from(cfg)
+    b = buffers_for(cfg)
+    M.moe_route(mc, inp.x, inp.w_gate, inp.logit_bias, b.logits, b.topk_idx, b.topk_gate, None,
+                b.ws)
+    M.moe_dispatch(mc, None, b.topk_idx, b.capacity, b.expert_offsets, b.route_rank,
+                   b.route_row, b.row_token, None, None, b.ws)
+    _placement_case(mc, b, inp.src_rank, cfg.n_ep, cfg.h, cfg.bytes_per_elem)

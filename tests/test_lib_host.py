@@ -247,3 +247,59 @@ def test_noalloc_dispatch_checks_on_the_host(lib):
         cfg = M.MoeCfg.make(A_fit + 1, 64, E, 1, 64, "bf16", 1.0)
         assert lib.moe_dispatch_noalloc(ctypes.byref(cfg), fake, fake, 8, fake, fake, fake, fake,
                                         None, None, None) == 5, E
+
+
+def test_place_experts_reaches_the_oracle_optimum(lib):
+    """moe_place_experts (host Hungarian method) against the oracle's
+    locality placement: the same number of local routes (the optimum is
+    unique, the map need not be), E / n_ep experts per rank, on random and
+    structured affinity matrices up to 256 experts."""
+    rng = np.random.default_rng(61)
+    cases = [(2, 2), (4, 2), (8, 4), (16, 16), (64, 8), (256, 8), (12, 3), (5, 1)]
+    for E, n in cases:
+        for kind in ("random", "tied", "local", "skewed"):
+            if kind == "random":
+                aff = rng.integers(0, 1000, (E, n))
+            elif kind == "tied":
+                aff = np.full((E, n), 7)
+            elif kind == "local":   # expert e gets its routes from rank perm(e) // (E/n)
+                perm = rng.permutation(E)
+                aff = rng.integers(0, 3, (E, n))
+                aff[np.arange(E), perm // (E // n)] += 500
+            else:                   # every rank prefers rank 0's experts
+                aff = rng.integers(0, 50, (E, n))
+                aff[:, 0] += rng.integers(0, 5000, E)
+            owner = M.moe_place_experts(aff.astype(np.int32), n)
+            assert sorted(np.bincount(owner, minlength=n).tolist()) == [E // n] * n
+            want = O.locality_placement(aff, n)
+            assert O.local_routes_under(aff, owner) == O.local_routes_under(aff, want), (E, n, kind)
+
+
+def test_place_experts_argument_checks(lib):
+    aff = np.zeros((6, 4), np.int32)
+    owner = (ctypes.c_int32 * 6)()
+    assert lib.moe_place_experts(ctypes.c_void_p(aff.ctypes.data), 6, 4, owner) == 1  # 6 % 4
+    assert lib.moe_place_experts(None, 6, 3, owner) == 1
+    aff[2, 1] = -1
+    assert lib.moe_place_experts(ctypes.c_void_p(aff.ctypes.data), 6, 3, owner) == 1
+    assert lib.moe_expert_rank_affinity(None, None, None, None, 2, None, None) == 1
+    cfg = M.MoeCfg.make(4, 64, 4, 2, 64, "bf16", 1.0)
+    assert lib.moe_expert_rank_affinity(ctypes.byref(cfg), None, None, None, 2, None, None) == 1
+    assert lib.moe_expert_rank_affinity(ctypes.byref(cfg), None, None, None, 65,
+                                        ctypes.c_void_p(256), None) == 1
+
+
+def test_fp8_ffn_checks_on_the_host(lib):
+    """moe_expert_ffn_fp8: bf16 only, and unsupported where the first GEMM
+    would take the tiled shape (rows per expert >= 384, F not a multiple of
+    128); both refused before any HIP call."""
+    fake = ctypes.c_void_p(256)
+    cfg32 = M.MoeCfg.make(64, 64, 4, 2, 64, "f32", 1.0)
+    assert lib.moe_expert_ffn_fp8(ctypes.byref(cfg32), 32, fake, fake, fake, fake, fake, fake,
+                                  fake, fake, fake, 0, None) == 5
+    cfg = M.MoeCfg.make(4096, 256, 4, 1, 192, "bf16", 1.0)   # 1024 rows per expert, F = 192
+    assert lib.moe_expert_ffn_fp8(ctypes.byref(cfg), 1024, fake, fake, fake, fake, fake, fake,
+                                  fake, fake, fake, 0, None) == 5
+    cfg = M.MoeCfg.make(64, 64, 4, 2, 64, "bf16", 1.0)
+    assert lib.moe_expert_ffn_fp8(ctypes.byref(cfg), 32, None, fake, fake, fake, fake, fake,
+                                  fake, fake, fake, 0, None) == 1

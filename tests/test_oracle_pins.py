@@ -605,3 +605,72 @@ def test_bias_update_bit_exact_against_the_pages_torch_expression():
         expert_bias.data += alpha * (mean_count - expert_count)
         got = O.expert_bias_update(bias, counts, alpha=alpha)
         assert np.array_equal(got, expert_bias.numpy().astype(np.float64)), (trial, E, T, alpha)
+
+
+# ------------------------------------------------ locality-aware placement
+def _all_equal_count_maps(E, n):
+    """Every expert -> rank map with E / n experts per rank (brute force)."""
+    import itertools
+    per = E // n
+    for owner in itertools.product(range(n), repeat=E):
+        if all(owner.count(r) == per for r in range(n)):
+            yield owner
+
+
+def test_placement_reaches_the_brute_force_optimum():
+    """[DSV3] 2.2 matches experts to devices on an affinity matrix; the
+    placement must keep E / n_ep experts per rank and reach the largest
+    number of local routes over all such maps (enumerated)."""
+    rng = np.random.default_rng(51)
+    for E, n in [(2, 2), (4, 2), (6, 2), (6, 3), (8, 4), (8, 2), (4, 4), (3, 1)]:
+        maps = list(_all_equal_count_maps(E, n))
+        for trial in range(6):
+            aff = rng.integers(0, 9, (E, n))
+            if trial == 0:
+                aff[:] = 3            # all maps tie
+            owner = O.locality_placement(aff, n)
+            assert sorted(np.bincount(owner, minlength=n).tolist()) == [E // n] * n
+            best = max(sum(int(aff[e, m[e]]) for e in range(E)) for m in maps)
+            assert O.local_routes_under(aff, owner) == best
+
+
+def test_affinity_and_locality_agree_with_the_page_contract():
+    """sum_e affinity[e, owner[e]] is the local-route count of [EP46]'s
+    dispatch-locality summary for any placement; the rows sum to the expert
+    loads and the whole matrix to the routes (accepted routes when route_row
+    is given)."""
+    rng = np.random.default_rng(52)
+    T, E, K, n = 300, 8, 2, 4
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+    src = rng.integers(0, n, T)
+    aff = O.expert_rank_affinity(idx, src, E, n)
+    assert aff.sum() == T * K
+    assert np.array_equal(aff.sum(axis=1), O.expert_loads(idx, E))
+    for owner in [np.arange(E) % n, O.locality_placement(aff, n), rng.integers(0, n, E)]:
+        loc = O.dispatch_locality(O.routes_from_idx(idx), src.tolist(),
+                                  {e: int(owner[e]) for e in range(E)}, 16)
+        assert O.local_routes_under(aff, owner) == loc["local_routes"]
+    cap = O.capacity(T * K, E, 0.8)
+    sl = O.slot_routes(idx, E, cap)
+    acc = O.expert_rank_affinity(idx, src, E, n, route_row=sl["route_row"])
+    assert acc.sum() == sl["R"]
+    assert np.array_equal(O.rank_loads(idx, sl["route_row"], np.arange(E) % n, n),
+                          np.bincount(np.arange(E) % n, weights=acc.sum(axis=1),
+                                      minlength=n).astype(np.int64))
+
+
+def test_placement_follows_rank_local_routing():
+    """Tokens of rank r route only to the experts of a hidden block of E / n
+    experts (a permuted local-heavy routing): the placement recovers that
+    block for every rank, so every route is local, where round robin keeps
+    only what the permutation happens to leave on each rank."""
+    rng = np.random.default_rng(53)
+    E, n, K, T = 8, 4, 2, 400
+    perm = rng.permutation(E)
+    home = {int(perm[e]): e // (E // n) for e in range(E)}  # expert -> hidden rank
+    src = rng.integers(0, n, T)
+    idx = np.stack([rng.permutation(perm[(E // n) * s:(E // n) * (s + 1)])[:K] for s in src])
+    aff = O.expert_rank_affinity(idx, src, E, n)
+    owner = O.locality_placement(aff, n)
+    assert O.local_routes_under(aff, owner) == T * K
+    assert all(int(owner[e]) == home[e] for e in range(E))
