@@ -109,7 +109,12 @@ def next_rows(M, bufs, torch, stream, x, weights, wl, reps=50):
     _, _, _, w1, b1, w2, b2 = weights
     bias = torch.zeros((cfg.E,), dtype=torch.float32, device="cuda")
     calls = {"bias_update_us": lambda: M.moe_bias_update(cfg, b.topk_idx, bias, 1e-3, None,
-                                                         stream)}
+                                                         stream),
+             # the dispatch with its row gather into x_disp (the step fuses the
+             # gather into the first GEMM instead)
+             "dispatch_gather_us": lambda: M.moe_dispatch(
+                 cfg, x, b.topk_idx, b.capacity, b.expert_offsets, b.route_rank, b.route_row,
+                 b.row_token, b.x_disp, None, b.ws, stream)}
     out = {}
     packed = w1 is not None and wl.dtype == "bf16"
     fp8_ffn = False
@@ -143,6 +148,11 @@ def next_rows(M, bufs, torch, stream, x, weights, wl, reps=50):
                 e.record(stream)
         torch.cuda.synchronize()
         out[name] = statistics.fmean(a.elapsed_time(e) for a, e in evs) * 1e3
+    R = int(b.expert_offsets[-1].item())
+    dbytes = algorithmic(wl, R, 0)["dispatch_bytes"]
+    gbs = dbytes / (out["dispatch_gather_us"] * 1e-6) / 1e9
+    out["dispatch_gather_hbm"] = {"gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
+                                  "algorithmic_bytes": dbytes}
     if fp8_ffn:
         offs = b.expert_offsets.cpu().tolist()
         e_nz = sum(1 for e in range(wl.E) if offs[e + 1] > offs[e])
@@ -215,9 +225,12 @@ def placement_row(M, torch, b, src_rank, n_ep, stream):
     cfg = b.cfg
     aff = torch.empty((cfg.E, n_ep), dtype=torch.int32, device="cuda")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
     with torch.cuda.stream(stream):
-        e0.record(stream)
         M.moe_expert_rank_affinity(cfg, b.topk_idx, None, src_rank, n_ep, aff, stream)
+        e0.record(stream)
+        for _ in range(reps):
+            M.moe_expert_rank_affinity(cfg, b.topk_idx, None, src_rank, n_ep, aff, stream)
         e1.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -232,7 +245,7 @@ def placement_row(M, torch, b, src_rank, n_ep, stream):
                        "cross_rank_dispatch_bytes": led["cross_rank_dispatch_bytes"],
                        "rank_balance": _rank_balance(led), "plan": M.moe_recommend_plan(led)}
     rows["owner"] = owner
-    rows["affinity_us"] = e0.elapsed_time(e1) * 1e3
+    rows["affinity_us"] = e0.elapsed_time(e1) * 1e3 / reps
     rows["placement_host_ms"] = t_place * 1e3
     return rows
 

@@ -10,7 +10,7 @@ namespace moe {
 
 namespace {
 
-template <bool VEC, int U>
+template <bool VEC, int U, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ route_row,
                                                       const float* __restrict__ gate,
@@ -18,7 +18,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int h, int TB) {
   __shared__ int s_row[kMaxTB * kMaxTopK];
   __shared__ float s_gate[kMaxTB * kMaxTopK];
-  combine_tokens<VEC, U>(blockIdx.x, y, route_row, gate, out, T, K, h, TB, s_row, s_gate);
+  combine_tokens<VEC, U, NT>(blockIdx.x, y, route_row, gate, out, T, K, h, TB, s_row, s_gate);
 }
 
 }  // namespace
@@ -26,9 +26,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_combine(const float* y, const int32_t* route_row, const float* gate,
                           float* out, int T, int K, int h, hipStream_t s) {
   if (T == 0 || h == 0) return hipSuccess;
-  const CombineShape c = combine_shape(T, h);
-  with_combine_variant(c, [&](auto vec, auto u) {
-    hipLaunchKernelGGL((combine_kernel<decltype(vec)::value, decltype(u)::value>),
+  const CombineShape c = combine_shape(T, K, h);
+  with_combine_variant(c, [&](auto vec, auto u, auto nt) {
+    hipLaunchKernelGGL((combine_kernel<decltype(vec)::value, decltype(u)::value,
+                                       decltype(nt)::value>),
                        dim3(c.grid), dim3(256), 0, s, y, route_row, gate, out, T, K, h, c.TB);
   });
   return hipGetLastError();

@@ -17,7 +17,7 @@
 namespace moe {
 
 
-// Expert outputs are read once: nontemporal loads.
+// Expert outputs are read once: nontemporal loads (large outputs, see NT).
 __device__ __forceinline__ float ntl(const float* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ float4 ntl(const float4* p) {
   const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
@@ -30,13 +30,15 @@ constexpr int kCombineLdsBytes = kMaxTB * kMaxTopK * 8;
 // Workgroup shape of the combine for T tokens of h fp32 values.  vec: rows
 // are read as float4; TB tokens per workgroup; U vectors per thread and trip.
 struct CombineShape {
-  bool vec;
+  bool vec, nt;
   int TB, U, grid;
 };
 
-inline CombineShape combine_shape(int T, int h) {
+inline CombineShape combine_shape(int T, int K, int h) {
   CombineShape c;
   c.vec = (h % 4) == 0;
+  // expert outputs of up to T*K rows: nontemporal reads above the LLC size
+  c.nt = (int64_t)T * K * h * 4 > ((int64_t)256 << 20);
   c.U = 4;
   const int hv = c.vec ? h / 4 : h;
   int TB = 256 * c.U / hv;  // about U vectors per thread
@@ -55,7 +57,10 @@ inline CombineShape combine_shape(int T, int h) {
 // at a time; the U loads of route k + 1 are issued before the FMAs of route
 // k, so one route's rows are always in flight while the previous one is
 // added.  s_row / s_gate: LDS of TB * K entries.
-template <bool VEC, int U>
+// NT: read the expert outputs with nontemporal loads (chosen when they
+// outgrow the 256 MB last-level cache; smaller ones are still resident there
+// from the expert GEMM that wrote them, and plain loads hit it).
+template <bool VEC, int U, bool NT>
 __device__ __forceinline__ void combine_tokens(int b, const float* __restrict__ y,
                                                const int32_t* __restrict__ route_row,
                                                const float* __restrict__ gate,
@@ -91,7 +96,7 @@ __device__ __forceinline__ void combine_tokens(int b, const float* __restrict__ 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       r[u] = s_row[tl[u] * K];
-      if (r[u] >= 0) v[u] = ntl(&yv[(size_t)r[u] * hv + c[u]]);
+      if (r[u] >= 0) v[u] = NT ? ntl(&yv[(size_t)r[u] * hv + c[u]]) : yv[(size_t)r[u] * hv + c[u]];
     }
     for (int k = 0; k < K; ++k) {
       V vn[U];
@@ -100,7 +105,8 @@ __device__ __forceinline__ void combine_tokens(int b, const float* __restrict__ 
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         rn[u] = k + 1 < K ? s_row[tl[u] * K + kn] : -1;
-        if (rn[u] >= 0) vn[u] = ntl(&yv[(size_t)rn[u] * hv + c[u]]);
+        if (rn[u] >= 0)
+          vn[u] = NT ? ntl(&yv[(size_t)rn[u] * hv + c[u]]) : yv[(size_t)rn[u] * hv + c[u]];
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -126,19 +132,26 @@ __device__ __forceinline__ void combine_tokens(int b, const float* __restrict__ 
   }
 }
 
-// Calls f(std::integral_constant<bool, VEC>, std::integral_constant<int, U>)
-// for the combine variant `c` selects (the set of instantiated variants).
+template <bool NT, class F>
+inline void with_combine_u(const CombineShape& c, F&& f) {
+  using std::integral_constant;
+  using N = integral_constant<bool, NT>;
+  if (!c.vec) return f(integral_constant<bool, false>(), integral_constant<int, 4>(), N());
+  switch (c.U) {
+    case 5: return f(integral_constant<bool, true>(), integral_constant<int, 5>(), N());
+    case 6: return f(integral_constant<bool, true>(), integral_constant<int, 6>(), N());
+    case 7: return f(integral_constant<bool, true>(), integral_constant<int, 7>(), N());
+    case 8: return f(integral_constant<bool, true>(), integral_constant<int, 8>(), N());
+    default: return f(integral_constant<bool, true>(), integral_constant<int, 4>(), N());
+  }
+}
+
+// Calls f(integral_constant<bool, VEC>, integral_constant<int, U>,
+// integral_constant<bool, NT>) for the combine variant `c` selects.
 template <class F>
 inline void with_combine_variant(const CombineShape& c, F&& f) {
-  using std::integral_constant;
-  if (!c.vec) return f(integral_constant<bool, false>(), integral_constant<int, 4>());
-  switch (c.U) {
-    case 5: return f(integral_constant<bool, true>(), integral_constant<int, 5>());
-    case 6: return f(integral_constant<bool, true>(), integral_constant<int, 6>());
-    case 7: return f(integral_constant<bool, true>(), integral_constant<int, 7>());
-    case 8: return f(integral_constant<bool, true>(), integral_constant<int, 8>());
-    default: return f(integral_constant<bool, true>(), integral_constant<int, 4>());
-  }
+  if (c.nt) return with_combine_u<true>(c, f);
+  return with_combine_u<false>(c, f);
 }
 
 }  // namespace moe

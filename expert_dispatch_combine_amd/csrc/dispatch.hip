@@ -180,7 +180,9 @@ __global__ __launch_bounds__(256) void slot_kernel(
 // the 256 threads; each thread issues U loads before their stores.  With a
 // scale (FP8 payload) each 16-byte vector of eight bf16 becomes eight E4M3
 // codes (8 bytes) of the destination row.
-template <int NR, int U>
+// NT: nontemporal stores of the dispatched rows (chosen when they outgrow the
+// 256 MB last-level cache, which could not keep them for the expert GEMM).
+template <int NR, int U, bool NT = false>
 __device__ __forceinline__ void copy_rows(const u32x4* __restrict__ x, void* __restrict__ xd,
                                           const int* dst, const int* src, int row_vecs,
                                           const float* __restrict__ q_scale) {
@@ -204,6 +206,7 @@ __device__ __forceinline__ void copy_rows(const u32x4* __restrict__ x, void* __r
     for (int u = 0; u < U; ++u) {
       if (to[u] < 0) continue;
       if (q_scale) ((uint2*)xd)[to[u]] = quantize8(v[u], scale);
+      else if (NT) __builtin_nontemporal_store(v[u], &((u32x4*)xd)[to[u]]);
       else ((u32x4*)xd)[to[u]] = v[u];
     }
   }
@@ -211,7 +214,7 @@ __device__ __forceinline__ void copy_rows(const u32x4* __restrict__ x, void* __r
 
 // x_disp[row] = x[row_token[row]] for row < R = offsets[E]; rows are
 // row_vecs 16-byte vectors long.  Each workgroup moves ROWS rows.
-template <int ROWS>
+template <int ROWS, bool NT>
 __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x,
                                                      const int32_t* __restrict__ row_token,
                                                      const int32_t* __restrict__ offsets,
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
     src[threadIdx.x] = r < R ? row_token[r] : 0;
   }
   __syncthreads();
-  copy_rows<ROWS, 8>(x, xd, dst, src, row_vecs, q_scale);
+  copy_rows<ROWS, 8, NT>(x, xd, dst, src, row_vecs, q_scale);
 }
 
 // The whole dispatch for A <= kSmallDispatchRoutes in one launch; block b
@@ -350,9 +353,14 @@ static hipError_t gather_rows(const void* x, const int32_t* row_token, const int
   if (vec) {
     constexpr int ROWS = 16;
     const int64_t grid = (r_max + ROWS - 1) / ROWS;
-    hipLaunchKernelGGL((gather_kernel<ROWS>), dim3((unsigned)grid), dim3(256), 0, s,
-                       (const u32x4*)x, row_token, offsets, E, (int)(row_bytes / 16), dst,
-                       q_scale);
+    if (r_max * row_bytes > ((int64_t)256 << 20))
+      hipLaunchKernelGGL((gather_kernel<ROWS, true>), dim3((unsigned)grid), dim3(256), 0, s,
+                         (const u32x4*)x, row_token, offsets, E, (int)(row_bytes / 16), dst,
+                         q_scale);
+    else
+      hipLaunchKernelGGL((gather_kernel<ROWS, false>), dim3((unsigned)grid), dim3(256), 0, s,
+                         (const u32x4*)x, row_token, offsets, E, (int)(row_bytes / 16), dst,
+                         q_scale);
   } else {
     hipLaunchKernelGGL(gather_bytes_kernel, dim3((unsigned)r_max), dim3(256), 0, s,
                        (const uint8_t*)x, row_token, offsets, E, row_bytes, (uint8_t*)dst);

@@ -88,28 +88,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-// OCP E4M3 code -> fp32, exactly (finite codes: the quantiser never writes
-// the NaN code).  A normal code's 4-bit exponent (bias 7) and 3-bit mantissa
-// move into the fp32 fields (exponent + 120); exponent 0 is subnormal,
-// m * 2^-9.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t em = c & 0x7Fu;
-  const float mag = em < 8u ? (float)em * 0x1p-9f : __uint_as_float((em << 20) + (120u << 23));
-  return (c & 0x80u) ? -mag : mag;
-}
-
 // eight E4M3 codes (lo: codes 0-3, hi: 4-7) -> eight bf16 of value * scale,
-// the receiver's dequantisation of the FP8 payload: the product of a 4-bit
-// and an 8-bit significand is exact in fp32 and is rounded once to bf16.
+// the receiver's dequantisation of the FP8 payload.  gfx950's packed
+// conversion widens two OCP E4M3 codes (bias 7, 3 mantissa bits, subnormals
+// m * 2^-9) to fp32 exactly; the product of a 4-bit and an 8-bit significand
+// is exact in fp32 and is rounded once to bf16.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4 dequant8(uint32_t lo, uint32_t hi, float scale) {
+  const f32x2v v0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+  const f32x2v v1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  const f32x2v v2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+  const f32x2v v3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
   u32x4 o;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t w = p < 2 ? lo : hi;
-    const int sh = 16 * (p & 1);
-    o[p] = pack_bf16x2(e4m3_to_f32((w >> sh) & 0xFFu) * scale,
-                       e4m3_to_f32((w >> (sh + 8)) & 0xFFu) * scale);
-  }
+  o[0] = pack_bf16x2(v0[0] * scale, v0[1] * scale);
+  o[1] = pack_bf16x2(v1[0] * scale, v1[1] * scale);
+  o[2] = pack_bf16x2(v2[0] * scale, v2[1] * scale);
+  o[3] = pack_bf16x2(v3[0] * scale, v3[1] * scale);
   return o;
 }
 

@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void ledger_partial_kernel(
 // part of the stage, blocks nled.. are the combine's workgroups.  The two
 // read the same routes and write disjoint outputs.
 constexpr int kLedgerPartRoutes = kSmallLedgerRoutes / kLedgerStageParts;
-template <bool VEC, int U>
+template <bool VEC, int U, bool NT>
 __global__ __launch_bounds__(256) void combine_ledger_kernel(
     const float* __restrict__ y, const int32_t* __restrict__ route_row,
     const float* __restrict__ gate, float* __restrict__ out, int T, int K, int h, int TB,
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void combine_ledger_kernel(
                                           nullptr, fin, nled, lds);
     return;
   }
-  combine_tokens<VEC, U>(blockIdx.x - nled, y, route_row, gate, out, T, K, h, TB, (int*)lds,
+  combine_tokens<VEC, U, NT>(blockIdx.x - nled, y, route_row, gate, out, T, K, h, TB, (int*)lds,
                          (float*)(lds + kMaxTB * kMaxTopK * 4));
 }
 
@@ -317,10 +317,11 @@ hipError_t launch_combine_ledger(const float* y, const int32_t* route_row, const
   char* fin = fin_dst ? (char*)fin_dst : w.fin;
   *final_area_out = fin;
   *final_bytes = w.fin_bytes;
-  const CombineShape c = combine_shape(T, h);
+  const CombineShape c = combine_shape(T, K, h);
   const int nled = (int)((A + kLedgerPartRoutes - 1) / kLedgerPartRoutes);
-  with_combine_variant(c, [&](auto vec, auto u) {
-    hipLaunchKernelGGL((combine_ledger_kernel<decltype(vec)::value, decltype(u)::value>),
+  with_combine_variant(c, [&](auto vec, auto u, auto nt) {
+    hipLaunchKernelGGL((combine_ledger_kernel<decltype(vec)::value, decltype(u)::value,
+                                              decltype(nt)::value>),
                        dim3(c.grid + nled), dim3(256), 0, s, y, route_row, gate, out, T, K, h,
                        c.TB, idx, src, owner, E, n_ep, nled, fin);
   });
