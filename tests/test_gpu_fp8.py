@@ -263,3 +263,40 @@ def test_fp8_step_end_to_end(cid):
     want = O.combine(Y_o, sl["route_row"], gate)
     got = b.out.cpu().numpy().astype(np.float64)
     assert np.max(np.abs(got - want)) <= 2e-2 * rms(want)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_fp8_ffn_widens_every_code(packed):
+    """Dispatched rows made of every finite E4M3 code (all 254 of them, both
+    signs, subnormals included), in several orders and scales: the first
+    GEMM's in-register widening gives the H and Y of the bf16 FFN on the rows
+    that moe_fp8_dequantize writes, bit for bit."""
+    banner(f"fp8 every code packed={packed}")
+    cfg = W.custom(T=96, h=256, E=3, K=1, F=128, cf=1.0, dtype="bf16", seed=77)
+    inp = custom_inputs(cfg)
+    mc = _mc(cfg)
+    cap = O.capacity(cfg.T, cfg.E, cfg.cf)
+    b = LayerBuffers(mc, cap)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)] + [0, 0x80], np.uint8)
+    rng = np.random.default_rng(78)
+    rows = np.stack([rng.permutation(codes) for _ in range(cfg.T)])
+    xq = torch.from_numpy(rows).cuda()
+    idx = (np.arange(cfg.T) % cfg.E).astype(np.int32)[:, None]
+    M.moe_dispatch(mc, None, torch.from_numpy(idx).cuda(), cap, b.expert_offsets, b.route_rank,
+                   b.route_row, b.row_token, None, None, b.ws)
+    w1, w2 = (pack_weights(mc, inp.w1, inp.w2) if packed else (inp.w1, inp.w2))
+    fn = M.moe_expert_ffn_packed if packed else M.moe_expert_ffn
+    for scale_v in (1.0, 2.0 ** -9, 0.0078125 * 3):
+        scale = torch.tensor([scale_v], dtype=torch.float32, device="cuda")
+        M.moe_fp8_dequantize(mc, cap, xq, scale, b.expert_offsets, b.x_disp)
+        torch.cuda.synchronize()
+        assert np.array_equal(b.x_disp[:cfg.T].double().cpu().numpy(),
+                              O.fp8_dequantize(rows, scale_v))
+        fn(mc, cap, b.x_disp, b.expert_offsets, w1, inp.b1, w2, inp.b2, b.h_buf, b.y)
+        torch.cuda.synchronize()
+        h_ref, y_ref = b.h_buf[:cfg.T].clone(), b.y[:cfg.T].clone()
+        b.h_buf.fill_(7.0)
+        M.moe_expert_ffn_fp8(mc, cap, xq, scale, b.expert_offsets, w1, inp.b1, w2, inp.b2,
+                             b.h_buf, b.y, packed)
+        torch.cuda.synchronize()
+        assert torch.equal(b.h_buf[:cfg.T], h_ref) and torch.equal(b.y[:cfg.T], y_ref)
