@@ -142,6 +142,8 @@ def next_rows(M, bufs, torch, stream, x, weights, wl, reps=50):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(reps)]
         with torch.cuda.stream(stream):
+            fn()  # first call (loads the kernel's code object) out of the timing
+            fn()
             for a, e in evs:
                 a.record(stream)
                 fn()
