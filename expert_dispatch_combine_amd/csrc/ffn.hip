@@ -43,6 +43,10 @@
 //    reads per MFMA of a 128 x 128 tiling) or 128 x 128 tiles at two per CU;
 //    global loads two chunks ahead, issued and staged a quarter per k-step
 //    between the MFMAs.
+//  * wide with weights in registers (packed weights, 512 or more rows per
+//    expert): 256 x 256 tiles, each wave all 256 rows x 64 weight rows of
+//    its own, its weight fragments loaded straight into registers; only the
+//    activations go through LDS.
 //
 // Scheduling is on the device (no host sync): every workgroup derives the
 // per-expert tile counts from `offsets`, maps its id to a logical tile with an
@@ -130,7 +134,7 @@ struct TileInfo {
 template <int BM, int BN>
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int N,
                                           TileInfo* sh, int tid) {
-  const int ntn = N / BN;
+  const int ntn = (N + BN - 1) / BN;
   if (tid < 64) {
     const int lane = tid;
     if (lane == 0) sh->e = -1;
@@ -860,6 +864,162 @@ __global__ __launch_bounds__(256, OCC) void wide_gemm_kernel(
 }
 
 // ==========================================================================
+// wide kernel with weights in registers: 256 activation rows x 256 weight rows
+// ==========================================================================
+// For the MFMA-bound shapes with packed weights.  Each of the 4 waves owns all
+// 256 rows of the tile and 64 weight rows of its own (8 x 2 MFMA tiles, the
+// 256 accumulator registers), so each weight fragment serves exactly one
+// wave: it goes from global memory straight into a register ring PD chunks
+// deep (one contiguous 1 KB load per fragment in the packed layout), and only
+// the activations are staged through LDS (double-buffered, XOR-swizzled):
+// per 16-wide k-step a wave reads 8 activation fragments for 16 MFMAs and no
+// weight fragment from LDS.  Activations of chunk c + 1 are loaded while
+// chunk c is computed and staged after its MFMAs; one barrier per chunk.
+// The tile's weight rows beyond N (N % 256 != 0, N % 64 == 0) leave whole
+// waves idle but present at the barriers.
+template <int EPI, int AB>
+__global__ __launch_bounds__(256, 1) void wide2_gemm_kernel(
+    const void* __restrict__ A, const uint16_t* __restrict__ W,
+    const float* __restrict__ bias, void* __restrict__ out,
+    const int32_t* __restrict__ offsets, int E, int N, int Kd,
+    const int32_t* __restrict__ rowmap, const float* __restrict__ ascale) {
+  constexpr int BM = 256, BN = 256, TM = 8, TN = 2, PD = 3, AQ = BM * 8 / 256;
+  constexpr int STAGE = BM * 64;  // bf16 elements of one activation stage
+  using AI = ActIn<AB>;
+  using AV = typename AI::V;
+  __shared__ __attribute__((aligned(16))) uint16_t act[2 * STAGE];
+  __shared__ TileInfo tinfo;
+  const int tid = threadIdx.x;
+  if (!find_tile<BM, BN>(offsets, E, N, &tinfo, tid)) return;
+  const int e = tinfo.e, row0 = tinfo.row0, row_end = tinfo.row_end, n0 = tinfo.n0;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, lg = lane >> 5;
+  const int nk = Kd / 64;
+  const int ncol = n0 + wave * 64;                          // this wave's first weight row
+  const bool active = __builtin_amdgcn_readfirstlane(ncol < N ? 1 : 0) != 0;
+
+  // weights: strip t of this wave, chunk c, k-step q at
+  // wp + t * sstr + c * PBLK + q * 512 (lane's 8 elements)
+  const uint16_t* wp = W + ((size_t)e * (N / 32) + (active ? ncol / 32 : 0)) * nk * PBLK + lane * 8;
+  const uint32_t sstr = (uint32_t)nk * PBLK;
+  u32x4 wr[PD][TN][4];
+
+  // activations: quad j of this thread is row (tid >> 3) + 32 j, quad tid & 7
+  const int sr = tid >> 3, sq = tid & 7;
+  // byte offsets from a per-tile base (the token matrix when rowmap gathers:
+  // the host keeps its byte count below 2^32)
+  const char* abase = (const char*)A + (rowmap ? 0 : (size_t)row0 * Kd * AB);
+  uint32_t aoff[AQ];
+#pragma unroll
+  for (int j = 0; j < AQ; ++j) {
+    const int row = min(row0 + sr + 32 * j, row_end - 1);
+    const uint32_t r = rowmap ? (uint32_t)rowmap[row] : (uint32_t)(row - row0);
+    aoff[j] = (r * (uint32_t)Kd + sq * 8) * AB;
+  }
+  const int adst = act_slot(sr, sq);            // + 32 * 64 * j for quad j
+  const float asc = AB == 1 ? *ascale : 0.0f;
+  // fragment of k-step s for MFMA tile tm: row 32 tm + li, quad 4 lg + s
+  const int fbase = li * 64, fsw = (li >> 1) & 7;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
+
+  // prologue: weights of chunks 0 .. PD-2, activations of chunk 0 -> LDS,
+  // activations of chunk 1 in flight
+  if (active) {
+#pragma unroll
+    for (int p = 0; p < PD - 1; ++p)
+      if (p < nk)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            wr[p][t][q] = __builtin_nontemporal_load(
+                (const u32x4*)(wp + t * sstr + (uint32_t)p * PBLK + q * 512));
+  }
+  AV areg[AQ];
+#pragma unroll
+  for (int j = 0; j < AQ; ++j) areg[j] = *(const AV*)(abase + aoff[j]);
+#pragma unroll
+  for (int j = 0; j < AQ; ++j) *(u32x4*)(act + adst + j * 32 * 64) = AI::widen(areg[j], asc);
+  if (nk > 1)
+#pragma unroll
+    for (int j = 0; j < AQ; ++j) areg[j] = *(const AV*)(abase + aoff[j] + 64u * AB);
+  __syncthreads();
+
+  // chunk c: weights of chunk c + PD - 1 into ring slot (SLOT + PD - 1) % PD,
+  // per k-step 8 activation fragments then 16 MFMAs (weights from slot SLOT),
+  // then chunk c + 1's activations into the other stage and chunk c + 2's
+  // loads issued; one barrier.
+#define MOE_W2_CHUNK(SLOT, c, REFILL, NEXT, NEXT2)                                          \
+  do {                                                                                      \
+    if (REFILL && active) {                                                                 \
+      _Pragma("unroll") for (int t = 0; t < TN; ++t)                                        \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q)                                       \
+          wr[((SLOT) + PD - 1) % PD][t][q] = __builtin_nontemporal_load(                    \
+              (const u32x4*)(wp + t * sstr + (uint32_t)((c) + PD - 1) * PBLK + q * 512));   \
+    }                                                                                       \
+    const uint16_t* st_ = act + ((c) & 1) * STAGE;                                          \
+    if (active) {                                                                           \
+      bf16x8 xf[2][TM];                                                                     \
+      _Pragma("unroll") for (int tm = 0; tm < TM; ++tm) xf[0][tm] =                         \
+          *(const bf16x8*)(st_ + fbase + tm * 32 * 64 + (((4 * lg) ^ fsw) << 3));           \
+      _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                       \
+        if (s < 3) {                                                                        \
+          _Pragma("unroll") for (int tm = 0; tm < TM; ++tm) xf[(s + 1) & 1][tm] =           \
+              *(const bf16x8*)(st_ + fbase + tm * 32 * 64 +                                 \
+                               (((4 * lg + s + 1) ^ fsw) << 3));                            \
+        }                                                                                   \
+        _Pragma("unroll") for (int tn = 0; tn < TN; ++tn) {                                 \
+          const bf16x8 wa = __builtin_bit_cast(bf16x8, wr[SLOT][tn][s]);                    \
+          _Pragma("unroll") for (int tm = 0; tm < TM; ++tm) acc[tm][tn] =                   \
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, xf[s & 1][tm], acc[tm][tn], 0, 0, \
+                                                      0);                                   \
+        }                                                                                   \
+      }                                                                                     \
+    }                                                                                       \
+    if (NEXT) {                                                                             \
+      uint16_t* nst_ = act + (((c) + 1) & 1) * STAGE;                                       \
+      _Pragma("unroll") for (int j = 0; j < AQ; ++j)                                        \
+        *(u32x4*)(nst_ + adst + j * 32 * 64) = AI::widen(areg[j], asc);                     \
+    }                                                                                       \
+    if (NEXT2) {                                                                            \
+      _Pragma("unroll") for (int j = 0; j < AQ; ++j) areg[j] =                              \
+          *(const AV*)(abase + aoff[j] + (uint32_t)((c) + 2) * 64u * AB);                   \
+    }                                                                                       \
+    __syncthreads();                                                                        \
+  } while (0)
+
+  int c0 = 0;
+  for (; c0 + 2 * PD <= nk; c0 += PD) {
+#pragma unroll
+    for (int p = 0; p < PD; ++p) MOE_W2_CHUNK(p, c0 + p, true, true, true);
+  }
+#pragma unroll
+  for (int p = 0; p < 2 * PD; ++p) {
+    const int c = c0 + p;
+    if (c < nk) MOE_W2_CHUNK(p % PD, c, c + PD - 1 < nk, c + 1 < nk, c + 2 < nk);
+  }
+#undef MOE_W2_CHUNK
+
+  if (!active) return;
+  const float* bptr = bias + (size_t)e * N;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int m = row0 + tm * 32 + li;
+    if (m >= row_end) continue;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+      store_tile<EPI>(acc[tm][tn], bptr, out, m, ncol + tn * 32 + lg * 4, N);
+  }
+}
+
+// ==========================================================================
 // weight packing: row-major [E, N, K] -> fragment blocks (see file header)
 // ==========================================================================
 __global__ __launch_bounds__(256) void pack_weights_kernel(const u32x4* __restrict__ src,
@@ -929,7 +1089,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
 // Upper bound of the tile count: sum_e ceil(rows_e / BM) <= r_max / BM + E,
 // rounded up to whole XCD rounds.
 int64_t grid_for(int64_t r_max, int BM, int E, int N, int BN) {
-  int64_t g = (r_max / BM + E) * (N / BN);
+  int64_t g = (r_max / BM + E) * ((N + BN - 1) / BN);
   return (g + NXCD - 1) / NXCD * NXCD;
 }
 
@@ -987,6 +1147,14 @@ hipError_t launch_wide(const GemmArgs& g) {
   return hipGetLastError();
 }
 
+template <int EPI, int AB>
+hipError_t launch_wide2(const GemmArgs& g) {
+  const int64_t grid = grid_for(g.r_max, 256, g.E, g.N, 256);
+  hipLaunchKernelGGL((wide2_gemm_kernel<EPI, AB>), dim3((unsigned)grid), dim3(256), 0, g.s, g.A,
+                     g.W, g.bias, g.out, g.offsets, g.E, g.N, g.Kd, g.rowmap, g.ascale);
+  return hipGetLastError();
+}
+
 template <int BN, int EPI, bool PK>
 hipError_t launch_tiled(const GemmArgs& g) {
   const int64_t grid = grid_for(g.r_max, TBM, g.E, g.N, BN);
@@ -998,8 +1166,11 @@ hipError_t launch_tiled(const GemmArgs& g) {
 
 // Shape choice.  rows_typ = the rows a typical expert holds, min(capacity,
 // ceil(A/E)); rows_max = min(capacity, A) bounds every expert.
-//  - rows_typ >= 512, N % 256 == 0, first GEMM (N = F, the long weight
-//    dim): MFMA bound, long segments -> wide kernel, 256 x 256 tiles.
+//  - packed weights, rows_typ >= 512 (MFMA bound, long segments): the wide
+//    kernel with weights in registers, both GEMMs (N a multiple of 64; the
+//    waves of a last, partial weight tile idle).
+//  - row-major weights, rows_typ >= 512, N % 256 == 0, first GEMM (N = F,
+//    the long weight dim): wide kernel, 256 x 256 tiles.
 //  - rows_typ >= 384, N % 128 == 0: wide kernel, 128 x 128 tiles, two
 //    workgroups per CU (finer tiles quantise better over 256 CUs; for the
 //    second GEMM they were as fast or faster than 256 x 256).
@@ -1008,10 +1179,12 @@ hipError_t launch_tiled(const GemmArgs& g) {
 //    rows_max <= 160 (each weight byte read once), else 128-row tiles; the
 //    weight-tile width 32*WN is the widest that still gives >= 256
 //    workgroups (one per CU), narrower ones split the k-chunk across waves.
-// Whether launch_gemm_auto takes the wide shape, whose loads address
-// activations by 32-bit element offsets.
-bool takes_wide_shape(bool first, int N, int64_t rows_typ) {
-  return (rows_typ >= 512 && N % 256 == 0 && first) || (rows_typ >= 384 && N % 128 == 0);
+// Whether launch_gemm_auto takes a wide shape, whose loads address
+// activations by 32-bit offsets (bytes with weights in registers, elements
+// in the LDS-staged one).
+bool takes_wide_shape(bool packed, bool first, int N, int64_t rows_typ) {
+  return (packed && rows_typ >= 512) || (rows_typ >= 512 && N % 256 == 0 && first) ||
+         (rows_typ >= 384 && N % 128 == 0);
 }
 
 // Whether the tiled shape serves this GEMM (it reads bf16 activations only).
@@ -1022,7 +1195,10 @@ bool takes_tiled_shape(int N, int64_t rows_typ) {
 template <int EPI, bool PK, int AB>
 hipError_t launch_gemm_auto(const GemmArgs& g, int64_t rows_typ, int64_t rows_max) {
   const int E = g.E, N = g.N;
-  if constexpr (EPI == 0)  // the 256 x 256 tiles serve the first GEMM only
+  if constexpr (PK)
+    if (rows_typ >= 512) return launch_wide2<EPI, AB>(g);
+  // the LDS-staged 256 x 256 tiles serve the first GEMM on row-major weights only
+  if constexpr (EPI == 0 && !PK)
     if (rows_typ >= 512 && N % 256 == 0) return launch_wide<256, 256, EPI, PK, 1, AB>(g);
   if (rows_typ >= 384 && N % 128 == 0) return launch_wide<128, 128, EPI, PK, 2, AB>(g);
   if (rows_typ >= 384) {
@@ -1054,8 +1230,8 @@ hipError_t launch_gemm_auto(const GemmArgs& g, int64_t rows_typ, int64_t rows_ma
 
 // row_token != nullptr: xd is the token matrix x (x_rows rows) and row r's
 // activations are x[row_token[r]].  GEMM1 gathers them in its own loads,
-// except in the wide shape when x holds 2^32 elements or more (its loads
-// take 32-bit offsets): then the rows are first copied into y's storage
+// except in a wide shape when x occupies 4 GiB or more (its loads take
+// 32-bit offsets): then the rows are first copied into y's storage
 // (R_max rows of h bf16 fit in the R_max x h fp32 of y), which GEMM1 reads
 // before GEMM2 overwrites it.
 template <bool PK>
@@ -1068,7 +1244,8 @@ hipError_t launch_ffn_bf16_t(const uint16_t* xd, const int32_t* row_token, int64
   const int64_t avg = (A + E - 1) / E;
   const int64_t rows_typ = avg < cap ? avg : cap;
   const int64_t rows_max = A < cap ? A : cap;
-  if (row_token && takes_wide_shape(true, F, rows_typ) && x_rows * h > (int64_t)UINT32_MAX) {
+  if (row_token && takes_wide_shape(PK, true, F, rows_typ) &&
+      x_rows * h * 2 > (int64_t)UINT32_MAX) {
     hipError_t err = launch_gather_rows(xd, row_token, offsets, E, (int64_t)h * 2, r_max, y, s);
     if (err != hipSuccess) return err;
     xd = (const uint16_t*)y;

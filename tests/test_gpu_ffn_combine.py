@@ -102,8 +102,10 @@ def test_ffn_every_row_full_size(cid):
 @pytest.mark.parametrize("packed", [False, True])
 def test_ffn_large_tiles_ragged(packed):
     """Experts of ~3300 rows (not a multiple of the row tile) and F = 4096:
-    the MFMA-bound tiled kernel on ragged segments; sampled rows (each
-    expert's first and last, both sides of a 256-row boundary, random)."""
+    the MFMA-bound wide kernels on ragged segments (weights in registers when
+    packed, LDS-staged 256 x 256 and 128 x 128 tiles when row-major); sampled
+    rows (each expert's first and last, both sides of a 256-row boundary,
+    random)."""
     banner(f"ffn tiled ragged packed={packed}")
     cfg = W.custom(T=16384, h=256, E=5, K=1, F=4096, cf=1.0, dtype="bf16", seed=31)
     inp = custom_inputs(cfg)
@@ -126,7 +128,9 @@ def test_ffn_large_tiles_ragged(packed):
                                           (3000, 128, 4, 1, 384, 1.3),
                                           (2200, 256, 3, 1, 512, 1.0),
                                           (3000, 64, 4, 1, 256, 1.3),
-                                          (2600, 192, 4, 1, 256, 1.3)])
+                                          (2600, 192, 4, 1, 256, 1.3),
+                                          (1800, 128, 4, 1, 384, 1.3),
+                                          (1800, 192, 4, 1, 448, 1.3)])
 @pytest.mark.parametrize("packed", [False, True])
 def test_ffn_ragged_segments(T, h, E, K, F, cf, packed):
     banner(f"ffn ragged T={T} h={h} E={E} K={K} F={F} packed={packed}")
@@ -142,10 +146,12 @@ def test_ffn_ragged_segments(T, h, E, K, F, cf, packed):
     (None, (2048, 768, 14, 1, 3072, 1.0), True),           # ragged, static tile map
     (None, (1000, 256, 4, 1, 320, 1.0), False),            # 250-row experts: tile search
     (None, (513, 64, 64, 6, 128, 1.0), True),              # many small / empty experts
-    (None, (2500, 192, 3, 1, 448, 1.5), True),             # long segments: tiled kernel
+    (None, (2500, 192, 3, 1, 448, 1.5), False),            # long segments: tiled kernel
+    (None, (2500, 192, 3, 1, 448, 1.5), True),             # weights in registers, partial tile
     (None, (4096, 256, 4, 1, 512, 1.0), False),            # wide kernel, 256 x 256 tiles
-    (None, (4096, 256, 4, 1, 512, 1.0), True),             # the same, packed weights
-    (None, (3000, 128, 4, 1, 384, 1.3), True),             # wide kernel, 128 x 128 tiles
+    (None, (4096, 256, 4, 1, 512, 1.0), True),             # weights in registers
+    (None, (1800, 128, 4, 1, 384, 1.3), True),             # wide kernel, 128 x 128 tiles
+    (None, (1800, 192, 4, 1, 448, 1.3), True),             # 450-row experts: tiled kernel
     (None, (1, 64, 1, 1, 64, 1.0), False),
     (1, None, False)])                                      # fp32: rows copied into y first
 def test_ffn_rows_equals_ffn_on_x_disp(cid, shape, packed):
