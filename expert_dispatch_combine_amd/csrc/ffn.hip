@@ -223,8 +223,13 @@ struct StreamShape {
   // chunks in the weight ring: 16 KB in flight per wave (8 KB when a wave
   // takes only 16 k of a chunk, to stay within the register budget)
   static constexpr int PD = OCC == 1 ? 8 : ((256 / KW) < 8 ? (256 / KW) : 8);
-  // activation register slots: chunk c + AD is loaded while chunk c computes
-  static constexpr int AD = OCC == 1 ? 4 : 2;
+  // activation register slots: chunk c + AD is loaded while chunk c computes.
+  // Loads complete in issue order, so the wait for chunk c + 1's activations
+  // also waits for every weight load issued before them: with AD = 4 those
+  // are weights of chunk c at the latest (already needed), with AD = 2 they
+  // include chunk c + 1's, which shortens the weight lookahead.  (AD = 4
+  // outgrows the registers of 160-row tiles at occupancy 2.)
+  static constexpr int AD = OCC == 1 || MT <= 4 ? 4 : 2;
   static constexpr int STAGE = BM * KC;      // bf16 elements of one LDS stage
   static constexpr int ACT_BYTES = 2 * STAGE * 2;
   static constexpr int RED_BYTES = (WK - 1) * WN * MT * 16 * 64 * 4;
