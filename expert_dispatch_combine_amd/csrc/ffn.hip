@@ -213,23 +213,30 @@ __device__ __forceinline__ int act_slot(int r, int q) { return r * 64 + ((q ^ ((
 // OCC = workgroups per CU the kernel is built for.  With OCC 1 (launches with
 // at most one workgroup per CU) each wave owns twice the registers, spent on
 // deeper prefetch: 8 weight chunks and 4 activation chunks in flight.
-template <int MT, int WN, int WK, int OCC>
+// TN = 32-row weight strips per wave.  With TN 2 or 4 (at OCC 1) each
+// staged activation chunk and each activation fragment read from LDS serves
+// TN times the weights, which divides the activation loads per weight byte
+// by TN; the ring then holds 4 (TN 2) or 2 (TN 4) chunks of all strips, the
+// same bytes in flight per CU as 8 waves with one strip and 4 chunks each.
+template <int MT, int WN, int WK, int OCC, int TN = 1>
 struct StreamShape {
   static constexpr int BM = 32 * MT;         // activation rows per workgroup
-  static constexpr int BN = 32 * WN;         // weight rows per workgroup
+  static constexpr int BN = 32 * WN * TN;    // weight rows per workgroup
   static constexpr int KC = 64;              // k per chunk (one LDS stage)
   static constexpr int KW = KC / WK;         // k per wave and chunk
   static constexpr int KSTEPS = KW / 16;     // MFMA k-steps per wave and chunk
   // chunks in the weight ring: 16 KB in flight per wave (8 KB when a wave
   // takes only 16 k of a chunk, to stay within the register budget)
-  static constexpr int PD = OCC == 1 ? 8 : ((256 / KW) < 8 ? (256 / KW) : 8);
+  static constexpr int PD = OCC == 1 ? (TN == 4 ? 2 : TN == 2 ? 4 : 8) : ((256 / KW) < 8 ? (256 / KW) : 8);
   // activation register slots: chunk c + AD is loaded while chunk c computes.
   // Loads complete in issue order, so the wait for chunk c + 1's activations
   // also waits for every weight load issued before them: with AD = 4 those
   // are weights of chunk c at the latest (already needed), with AD = 2 they
   // include chunk c + 1's, which shortens the weight lookahead.  (AD = 4
-  // outgrows the registers of 160-row tiles at occupancy 2.)
-  static constexpr int AD = OCC == 1 || MT <= 4 ? 4 : 2;
+  // outgrows the registers of 160-row tiles at occupancy 2, and of four
+  // strips per wave; with TN 4 the ring is 2 chunks deep, so the weights
+  // issued before chunk c + 1's activations are again those of chunk c.)
+  static constexpr int AD = TN == 4 ? 2 : OCC == 1 || MT <= 4 ? 4 : 2;
   static constexpr int STAGE = BM * KC;      // bf16 elements of one LDS stage
   static constexpr int ACT_BYTES = 2 * STAGE * 2;
   static constexpr int RED_BYTES = (WK - 1) * WN * MT * 16 * 64 * 4;
@@ -248,13 +255,14 @@ struct StreamShape {
 // done by the loads themselves: A is then the token matrix x).
 // AB: activation bytes per element, 2 (bf16) or 1 (E4M3 codes, widened to
 // bf16 x *ascale before they are staged in LDS).
-template <int MT, int WN, int WK, int EPI, bool PK, int OCC, int AB>
+template <int MT, int WN, int WK, int EPI, bool PK, int OCC, int AB, int TN>
 __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     const void* __restrict__ A, const uint16_t* __restrict__ W,
     const float* __restrict__ bias, void* __restrict__ out,
     const int32_t* __restrict__ offsets, int E, int N, int Kd, int one_rt,
     const int32_t* __restrict__ rowmap, const float* __restrict__ ascale) {
-  using S = StreamShape<MT, WN, WK, OCC>;
+  using S = StreamShape<MT, WN, WK, OCC, TN>;
+  static_assert(TN == 1 || WK == 1, "strips per wave without a k split");
   using AI = ActIn<AB>;
   using AV = typename AI::V;
   static_assert(S::PD % S::AD == 0 && S::PD % 2 == 0, "ring sizes");
@@ -292,17 +300,20 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
   constexpr int CSTR = PK ? PBLK : S::KC;
   constexpr int QSTR = PK ? 512 : 8;
   if (PK)
-    wp = W + ((size_t)e * (N / 32) + (n0 + wn * 32) / 32) * nchunks * PBLK +
+    wp = W + ((size_t)e * (N / 32) + (n0 + wn * TN * 32) / 32) * nchunks * PBLK +
          (kw * S::KSTEPS * 64 + lane) * 8;
   else
-    wp = W + ((size_t)e * N + n0 + wn * 32 + li) * Kd + kw * S::KW + lg * (S::KW / 2);
-  u32x4 wr[S::PD][S::KSTEPS];
+    wp = W + ((size_t)e * N + n0 + wn * TN * 32 + li) * Kd + kw * S::KW + lg * (S::KW / 2);
+  const size_t tstr = PK ? (size_t)nchunks * PBLK : (size_t)32 * Kd;  // next strip
+  u32x4 wr[S::PD][TN][S::KSTEPS];
 #pragma unroll
   for (int p = 0; p < S::PD - 1; ++p)
     if (p < nchunks)
 #pragma unroll
-      for (int q = 0; q < S::KSTEPS; ++q)
-        wr[p][q] = __builtin_nontemporal_load((const u32x4*)(wp + p * CSTR + q * QSTR));
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int q = 0; q < S::KSTEPS; ++q)
+          wr[p][t][q] = __builtin_nontemporal_load((const u32x4*)(wp + t * tstr + p * CSTR + q * QSTR));
   if (one_rt) {
     row0 = offsets[e];
     row_end = offsets[e + 1];
@@ -333,11 +344,13 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
       afrag[tm][s] = act_slot(r, q);
     }
 
-  f32x16 acc[MT];
+  f32x16 acc[MT][TN];
 #pragma unroll
   for (int tm = 0; tm < MT; ++tm)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[tm][r] = 0.f;
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tm][t][r] = 0.f;
 
   // activations: chunk 0 straight into LDS stage 0, chunks 1 .. AD-1 into
   // register slots; chunk c+AD is always in flight while chunk c is computed
@@ -370,9 +383,10 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
           *(const AV*)(ap[j] + ((c) + S::AD) * S::KC * AB);                           \
     }                                                                                 \
     if (REFILL) {                                                                     \
-      _Pragma("unroll") for (int q = 0; q < S::KSTEPS; ++q)                           \
-        wr[((SLOT) + S::PD - 1) % S::PD][q] =                                         \
-            __builtin_nontemporal_load((const u32x4*)(wp + ((c) + S::PD - 1) * CSTR + q * QSTR)); \
+      _Pragma("unroll") for (int t = 0; t < TN; ++t)                                  \
+        _Pragma("unroll") for (int q = 0; q < S::KSTEPS; ++q)                         \
+          wr[((SLOT) + S::PD - 1) % S::PD][t][q] = __builtin_nontemporal_load(        \
+              (const u32x4*)(wp + t * tstr + ((c) + S::PD - 1) * CSTR + q * QSTR));   \
     }                                                                                 \
     if constexpr (OCC == 1) {                                                         \
       /* one wave per SIMD: nothing else hides LDS latency, so every fragment */      \
@@ -383,18 +397,20 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
         _Pragma("unroll") for (int tm = 0; tm < MT; ++tm) xf_[s][tm] =                \
             *(const bf16x8*)(stage_ + afrag[tm][s]);                                  \
       __builtin_amdgcn_sched_barrier(0);                                              \
-      _Pragma("unroll") for (int s = 0; s < S::KSTEPS; ++s) {                         \
-        const bf16x8 wa = __builtin_bit_cast(bf16x8, wr[SLOT][s]);                    \
-        _Pragma("unroll") for (int tm = 0; tm < MT; ++tm)                             \
-          acc[tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, xf_[s][tm], acc[tm],   \
-                                                            0, 0, 0);                 \
-      }                                                                               \
+      _Pragma("unroll") for (int s = 0; s < S::KSTEPS; ++s)                           \
+        _Pragma("unroll") for (int t = 0; t < TN; ++t) {                              \
+          const bf16x8 wa = __builtin_bit_cast(bf16x8, wr[SLOT][t][s]);               \
+          _Pragma("unroll") for (int tm = 0; tm < MT; ++tm)                           \
+            acc[tm][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, xf_[s][tm],       \
+                                                                 acc[tm][t], 0, 0, 0); \
+        }                                                                             \
     } else {                                                                          \
       _Pragma("unroll") for (int s = 0; s < S::KSTEPS; ++s) {                         \
-        const bf16x8 wa = __builtin_bit_cast(bf16x8, wr[SLOT][s]);                    \
         _Pragma("unroll") for (int tm = 0; tm < MT; ++tm) {                           \
           const bf16x8 xb = *(const bf16x8*)(stage_ + afrag[tm][s]);                  \
-          acc[tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, xb, acc[tm], 0, 0, 0); \
+          _Pragma("unroll") for (int t = 0; t < TN; ++t)                              \
+            acc[tm][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                     \
+                __builtin_bit_cast(bf16x8, wr[SLOT][t][s]), xb, acc[tm][t], 0, 0, 0); \
         }                                                                             \
       }                                                                               \
     }                                                                                 \
@@ -431,7 +447,7 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
       for (int tm = 0; tm < MT; ++tm)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          red[((((kw - 1) * WN + wn) * MT + tm) * 16 + r) * 64 + lane] = acc[tm][r];
+          red[((((kw - 1) * WN + wn) * MT + tm) * 16 + r) * 64 + lane] = acc[tm][0][r];
     }
     __syncthreads();
     if (kw == 0) {
@@ -441,7 +457,7 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
         for (int tm = 0; tm < MT; ++tm)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            acc[tm][r] += red[((((k2 - 1) * WN + wn) * MT + tm) * 16 + r) * 64 + lane];
+            acc[tm][0][r] += red[((((k2 - 1) * WN + wn) * MT + tm) * 16 + r) * 64 + lane];
     }
   }
 
@@ -451,11 +467,13 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
   constexpr int ESZ = EPI == 0 ? 2 : 4;
   constexpr int ROWB = S::OUT_ROW_BYTES(ESZ);
   constexpr int CPR = S::BN * ESZ / 16;  // 16-byte chunks per output row
-  float4 bq[4];
+  float4 bq[TN][4];
   {
-    const float* bptr = bias + (size_t)e * N + n0 + wn * 32 + lg * 4;
+    const float* bptr = bias + (size_t)e * N + n0 + wn * TN * 32 + lg * 4;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bq[q] = *(const float4*)(bptr + q * 8);
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bq[t][q] = *(const float4*)(bptr + t * 32 + q * 8);
   }
   char* tile = lds;
   if constexpr (ONE_PASS) {
@@ -464,11 +482,13 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
 #pragma unroll
       for (int tm = 0; tm < MT; ++tm) {
         if (row0 + tm * 32 >= row_end) break;  // uniform
-        char* rowp = tile + (tm * 32 + li) * ROWB + (wn * 32 + lg * 4) * ESZ;
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float v0 = acc[tm][4 * q + 0] + bq[q].x, v1 = acc[tm][4 * q + 1] + bq[q].y;
-          const float v2 = acc[tm][4 * q + 2] + bq[q].z, v3 = acc[tm][4 * q + 3] + bq[q].w;
+          char* rowp = tile + (tm * 32 + li) * ROWB + ((wn * TN + t) * 32 + lg * 4) * ESZ;
+          const float v0 = acc[tm][t][4 * q + 0] + bq[t][q].x, v1 = acc[tm][t][4 * q + 1] + bq[t][q].y;
+          const float v2 = acc[tm][t][4 * q + 2] + bq[t][q].z, v3 = acc[tm][t][4 * q + 3] + bq[t][q].w;
           if (EPI == 0) {
             uint2 pk;
             pk.x = pack_bf16x2(gelu_tanh_bf16(v0), gelu_tanh_bf16(v1));
@@ -497,11 +517,13 @@ __global__ __launch_bounds__(256, OCC) void stream_gemm_kernel(
     if (row0 + tm * 32 >= row_end) break;  // uniform
     __syncthreads();  // LDS free: previous pass copied out / reduction read
     if (kw == 0) {
-      char* rowp = tile + li * ROWB + (wn * 32 + lg * 4) * ESZ;
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float v0 = acc[tm][4 * q + 0] + bq[q].x, v1 = acc[tm][4 * q + 1] + bq[q].y;
-        const float v2 = acc[tm][4 * q + 2] + bq[q].z, v3 = acc[tm][4 * q + 3] + bq[q].w;
+        char* rowp = tile + li * ROWB + ((wn * TN + t) * 32 + lg * 4) * ESZ;
+        const float v0 = acc[tm][t][4 * q + 0] + bq[t][q].x, v1 = acc[tm][t][4 * q + 1] + bq[t][q].y;
+        const float v2 = acc[tm][t][4 * q + 2] + bq[t][q].z, v3 = acc[tm][t][4 * q + 3] + bq[t][q].w;
         if (EPI == 0) {
           uint2 pk;
           pk.x = pack_bf16x2(gelu_tanh_bf16(v0), gelu_tanh_bf16(v1));
@@ -1114,13 +1136,13 @@ struct GemmArgs {
   hipStream_t s;
 };
 
-template <int MT, int WN, int WK, int EPI, bool PK, int OCC, int AB>
+template <int MT, int WN, int WK, int EPI, bool PK, int OCC, int AB, int TN = 1>
 hipError_t launch_stream(const GemmArgs& g, bool static_map) {
   // static_map: every expert's rows fit one row tile (see the kernel)
   const int one_rt = static_map ? 1 : 0;
-  const int64_t grid = one_rt ? ((int64_t)g.E * (g.N / (32 * WN)) + NXCD - 1) / NXCD * NXCD
-                              : grid_for(g.r_max, 32 * MT, g.E, g.N, 32 * WN);
-  hipLaunchKernelGGL((stream_gemm_kernel<MT, WN, WK, EPI, PK, OCC, AB>), dim3((unsigned)grid),
+  const int64_t grid = one_rt ? ((int64_t)g.E * (g.N / (32 * WN * TN)) + NXCD - 1) / NXCD * NXCD
+                              : grid_for(g.r_max, 32 * MT, g.E, g.N, 32 * WN * TN);
+  hipLaunchKernelGGL((stream_gemm_kernel<MT, WN, WK, EPI, PK, OCC, AB, TN>), dim3((unsigned)grid),
                      dim3(256), 0, g.s, g.A, g.W, g.bias, g.out, g.offsets, g.E, g.N, g.Kd, one_rt,
                      g.rowmap, g.ascale);
   return hipGetLastError();
@@ -1135,7 +1157,13 @@ hipError_t launch_stream_occ(const GemmArgs& g, bool occ1, bool static_map) {
 }
 
 template <int MT, int EPI, bool PK, int AB>
-hipError_t launch_stream_mt(const GemmArgs& g, int wn, bool occ1, bool static_map) {
+hipError_t launch_stream_mt(const GemmArgs& g, int wn, bool occ1, bool static_map, int tn) {
+  if constexpr (MT <= 4) {
+    // (four strips fit the registers with packed weights only)
+    if constexpr (PK)
+      if (tn == 4) return launch_stream<MT, 4, 1, EPI, PK, 1, AB, 4>(g, static_map);
+    if (tn >= 2) return launch_stream<MT, 4, 1, EPI, PK, 1, AB, 2>(g, static_map);
+  }
   if (wn == 4) return launch_stream_occ<MT, 4, 1, EPI, PK, AB>(g, occ1, static_map);
   // the 4-way k split keeps MT <= 3 (its reduction and ring outgrow the registers)
   if (wn == 2 || MT >= 4) return launch_stream_occ<MT, 2, 2, EPI, PK, AB>(g, occ1, static_map);
@@ -1184,6 +1212,10 @@ hipError_t launch_tiled(const GemmArgs& g) {
 //    rows_max <= 160 (each weight byte read once), else 128-row tiles; the
 //    weight-tile width 32*WN is the widest that still gives >= 256
 //    workgroups (one per CU), narrower ones split the k-chunk across waves.
+//    Tiles of up to 128 rows take four weight strips per wave instead
+//    (512-wide weight tiles, one workgroup per CU) with packed weights when
+//    N is a multiple of 512 and that leaves at least 256 tiles, else two
+//    (256-wide) under the same rule.
 // Whether launch_gemm_auto takes a wide shape, whose loads address
 // activations by 32-bit offsets (bytes with weights in registers, elements
 // in the LDS-staged one).
@@ -1224,12 +1256,20 @@ hipError_t launch_gemm_auto(const GemmArgs& g, int64_t rows_typ, int64_t rows_ma
   else if (mtiles * (N / 64) >= 256 || mt >= 4) wn = 2;
   // at most one workgroup of work per CU: build for occupancy 1 and prefetch deeper
   const bool occ1 = mtiles * (N / (32 * wn)) <= 256;
+  // two or four weight strips per wave (256 or 512 weight rows per
+  // workgroup, one workgroup per CU) where that still gives every CU a
+  // workgroup
+  int tn = 1;
+  if (mt <= 4 && wn == 4) {
+    if (PK && N % 512 == 0 && mtiles * (N / 512) >= 256) tn = 4;
+    else if (N % 256 == 0 && mtiles * (N / 256) >= 256) tn = 2;
+  }
   switch (mt) {
-    case 1: return launch_stream_mt<1, EPI, PK, AB>(g, wn, occ1, one_rt);
-    case 2: return launch_stream_mt<2, EPI, PK, AB>(g, wn, occ1, one_rt);
-    case 3: return launch_stream_mt<3, EPI, PK, AB>(g, wn, occ1, one_rt);
-    case 4: return launch_stream_mt<4, EPI, PK, AB>(g, wn, occ1, one_rt);
-    default: return launch_stream_mt<5, EPI, PK, AB>(g, wn, occ1, one_rt);
+    case 1: return launch_stream_mt<1, EPI, PK, AB>(g, wn, occ1, one_rt, tn);
+    case 2: return launch_stream_mt<2, EPI, PK, AB>(g, wn, occ1, one_rt, tn);
+    case 3: return launch_stream_mt<3, EPI, PK, AB>(g, wn, occ1, one_rt, tn);
+    case 4: return launch_stream_mt<4, EPI, PK, AB>(g, wn, occ1, one_rt, tn);
+    default: return launch_stream_mt<5, EPI, PK, AB>(g, wn, occ1, one_rt, tn);
   }
 }
 

@@ -130,7 +130,10 @@ def test_ffn_large_tiles_ragged(packed):
                                           (3000, 64, 4, 1, 256, 1.3),
                                           (2600, 192, 4, 1, 256, 1.3),
                                           (1800, 128, 4, 1, 384, 1.3),
-                                          (1800, 192, 4, 1, 448, 1.3)])
+                                          (1800, 192, 4, 1, 448, 1.3),
+                                          (4096, 256, 16, 1, 4096, 1.25),
+                                          (4096, 256, 16, 1, 2304, 1.25),
+                                          (4096, 4096, 16, 1, 256, 1.25)])
 @pytest.mark.parametrize("packed", [False, True])
 def test_ffn_ragged_segments(T, h, E, K, F, cf, packed):
     banner(f"ffn ragged T={T} h={h} E={E} K={K} F={F} packed={packed}")
@@ -152,6 +155,7 @@ def test_ffn_ragged_segments(T, h, E, K, F, cf, packed):
     (None, (4096, 256, 4, 1, 512, 1.0), True),             # weights in registers
     (None, (1800, 128, 4, 1, 384, 1.3), True),             # wide kernel, 128 x 128 tiles
     (None, (1800, 192, 4, 1, 448, 1.3), True),             # 450-row experts: tiled kernel
+    (None, (4096, 256, 16, 1, 4096, 1.25), True),          # two weight strips per wave
     (None, (1, 64, 1, 1, 64, 1.0), False),
     (1, None, False)])                                      # fp32: rows copied into y first
 def test_ffn_rows_equals_ffn_on_x_disp(cid, shape, packed):
