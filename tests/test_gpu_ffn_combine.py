@@ -144,6 +144,22 @@ def test_ffn_ragged_segments(T, h, E, K, F, cf, packed):
     _check_rows(inp, sl, b, np.arange(sl["R"]))
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_ffn_static_map_with_empty_experts(packed):
+    """Every expert's rows fit one 128-row tile (the static tile map) and a
+    strong router bias leaves many experts empty and caps the hot ones: the
+    multi-strip streaming kernels (four strips in GEMM1 with packed weights,
+    two in GEMM2) on empty, full and partial experts; every accepted row."""
+    banner(f"ffn static map, empty experts, packed={packed}")
+    cfg = W.custom(T=4096, h=256, E=256, K=8, F=2048, cf=1.0, dtype="bf16", zipf_s=3.0, seed=77)
+    inp = custom_inputs(cfg)
+    _, _, cap, sl = _oracle_dispatch(inp)
+    rows = np.diff(sl["expert_offsets"])
+    assert cap == 128 and (rows == 0).sum() > 0 and (rows == cap).sum() > 0
+    b = _run_ffn(inp, cap, sl, packed)
+    _check_rows(inp, sl, b, np.arange(sl["R"]))
+
+
 @pytest.mark.parametrize("cid,shape,packed", [
     (2, None, True), (2, None, False),                     # gather in the streaming loads
     (None, (2048, 768, 14, 1, 3072, 1.0), True),           # ragged, static tile map
