@@ -78,7 +78,7 @@ def parse():
     p.add_argument("--no-next-rows", action="store_true",
                    help="skip the timings of the entry points beyond the layer step (bias "
                         "update, FP8 payload, routing scenarios), e.g. under a profiler")
-    p.add_argument("--cpu-experts", type=int, default=16,
+    p.add_argument("--cpu-experts", type=int, default=96,
                    help="experts whose FFN the CPU-oracle baseline runs (evenly spaced; the "
                         "FFN time is scaled to all accepted rows)")
     return p.parse_args()
