@@ -315,7 +315,8 @@ int moe_expert_ffn_fp8(const moe_cfg* cfg, int64_t capacity, const uint8_t* x_di
   if (st != MOE_OK) return st;
   if (cfg->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (capacity < 0) return MOE_ERR_INVALID_ARG;
-  if (!ffn_fp8_supported(cfg->E, cfg->F, routes_of(cfg), capacity)) return MOE_ERR_UNSUPPORTED;
+  if (!ffn_fp8_supported(cfg->E, cfg->F, routes_of(cfg), capacity, packed != 0))
+    return MOE_ERR_UNSUPPORTED;
   const int64_t rmax = rows_max(cfg, capacity);
   if (rmax == 0) return MOE_OK;
   if (!x_disp_q || !scale || !expert_offsets || !w1 || !b1 || !w2 || !b2 || !h_buf || !y)

@@ -1337,9 +1337,11 @@ hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* row_token, int64_t
                                   F, A, cap, r_max, s);
 }
 
-bool ffn_fp8_supported(int E, int F, int64_t A, int64_t cap) {
+bool ffn_fp8_supported(int E, int F, int64_t A, int64_t cap, bool packed) {
   const int64_t avg = E > 0 ? (A + E - 1) / E : 0;
-  return !takes_tiled_shape(F, avg < cap ? avg : cap);
+  const int64_t rows_typ = avg < cap ? avg : cap;
+  if (packed && rows_typ >= 512) return true;  // weights in registers: any N % 64 == 0
+  return !takes_tiled_shape(F, rows_typ);
 }
 
 hipError_t launch_ffn_fp8(const uint8_t* xq, const float* scale, const int32_t* offsets,

@@ -215,7 +215,7 @@ hipError_t launch_ffn_bf16(const uint16_t* xd, const int32_t* row_token, int64_t
 // The expert FFN on the FP8 payload: GEMM1 reads E4M3 codes xq [R_max, h] and
 // widens them to bf16 x *scale while staging them.  ffn_fp8_supported: false
 // where GEMM1 would take the tiled shape (bf16 activations only).
-bool ffn_fp8_supported(int E, int F, int64_t A, int64_t cap);
+bool ffn_fp8_supported(int E, int F, int64_t A, int64_t cap, bool packed);
 hipError_t launch_ffn_fp8(const uint8_t* xq, const float* scale, const int32_t* offsets,
                           const uint16_t* w1, const float* b1, const uint16_t* w2,
                           const float* b2, uint16_t* hbuf, float* y, int E, int h, int F,

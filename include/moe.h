@@ -171,7 +171,8 @@ int moe_fp8_dequantize(const moe_cfg* cfg, int64_t capacity, const uint8_t* x_di
  * device fp32 from moe_fp8_scale; the other arguments as for moe_expert_ffn.
  * bf16 only; MOE_ERR_UNSUPPORTED also where the first GEMM's rows per
  * expert (min(capacity, ceil(T*K/E))) reach 384 while F is not a multiple of
- * 128 (a shape whose kernel reads bf16 activations only). */
+ * 128 (a shape whose kernel reads bf16 activations only), unless the weights
+ * are packed and those rows reach 512. */
 int moe_expert_ffn_fp8(const moe_cfg* cfg, int64_t capacity, const uint8_t* x_disp_q,
                        const float* scale, const int32_t* expert_offsets, const void* w1,
                        const float* b1, const void* w2, const float* b2, void* h_buf, float* y,

@@ -185,6 +185,7 @@ def test_fp8_layer_end_to_end():
     (None, (4096, 256, 4, 1, 512, 1.0), False),        # wide 256 x 256 first GEMM
     (None, (1800, 128, 4, 1, 384, 1.3), True),         # wide 128 x 128, 450-row experts
     (None, (4096, 256, 16, 1, 4096, 1.25), True),      # two weight strips per wave, tile search
+    (None, (4096, 256, 4, 1, 192, 1.0), True),         # weights in registers, F = 192
     (None, (1000, 256, 4, 1, 320, 1.0), False),        # streaming with the tile search
     (None, (513, 64, 64, 6, 128, 1.0), True)])         # many small / empty experts
 def test_fp8_ffn_equals_ffn_on_dequantised_rows(cid, shape, packed):

@@ -292,7 +292,8 @@ def test_place_experts_argument_checks(lib):
 def test_fp8_ffn_checks_on_the_host(lib):
     """moe_expert_ffn_fp8: bf16 only, and unsupported where the first GEMM
     would take the tiled shape (rows per expert >= 384, F not a multiple of
-    128); both refused before any HIP call."""
+    128, row-major weights or fewer than 512 rows per expert); both refused
+    before any HIP call."""
     fake = ctypes.c_void_p(256)
     cfg32 = M.MoeCfg.make(64, 64, 4, 2, 64, "f32", 1.0)
     assert lib.moe_expert_ffn_fp8(ctypes.byref(cfg32), 32, fake, fake, fake, fake, fake, fake,
@@ -300,6 +301,9 @@ def test_fp8_ffn_checks_on_the_host(lib):
     cfg = M.MoeCfg.make(4096, 256, 4, 1, 192, "bf16", 1.0)   # 1024 rows per expert, F = 192
     assert lib.moe_expert_ffn_fp8(ctypes.byref(cfg), 1024, fake, fake, fake, fake, fake, fake,
                                   fake, fake, fake, 0, None) == 5
+    cfg = M.MoeCfg.make(1800, 256, 4, 1, 192, "bf16", 1.3)   # 450 rows per expert, packed
+    assert lib.moe_expert_ffn_fp8(ctypes.byref(cfg), 585, fake, fake, fake, fake, fake, fake,
+                                  fake, fake, fake, 1, None) == 5
     cfg = M.MoeCfg.make(64, 64, 4, 2, 64, "bf16", 1.0)
     assert lib.moe_expert_ffn_fp8(ctypes.byref(cfg), 32, None, fake, fake, fake, fake, fake,
                                   fake, fake, fake, 0, None) == 1
