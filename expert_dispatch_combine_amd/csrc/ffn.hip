@@ -21,20 +21,20 @@
 //    one linear stream, which is what HBM serves at full rate (row-major
 //    fragments touch 32 rows x 32 bytes per load and run ~30% slower).
 //
-// Three kernel shapes, chosen per launch on the host:
+// Four kernel shapes, chosen per launch on the host:
 //  * streaming (rows per expert up to a few hundred: weight-bandwidth bound).
 //    A workgroup takes ALL rows of one expert (up to 160, in 32-row MFMA
-//    tiles) and 32*WN weight rows, so each weight byte crosses HBM once.
+//    tiles) and 32*WN*TN weight rows, so each weight byte crosses HBM once.
 //    Weights are read once, with nontemporal loads (streamed past the caches
 //    that keep the activations), and the fp32 outputs of the second GEMM are
 //    written with nontemporal stores.
 //    Weights go straight from global memory into a register ring PD chunks
-//    deep (no LDS); activations are shared by the 4 waves through a
-//    double-buffered, XOR-swizzled LDS tile, loaded two chunks ahead (four
-//    when a launch has at most one workgroup per CU).  WK
-//    waves split each 64-wide k-chunk when the weight dim is too short to
-//    give the chip enough work; their partial sums are added in LDS in a
-//    fixed order.
+//    deep (no LDS), TN 32-row strips per wave (up to four where a launch
+//    still gives every CU a workgroup); activations are shared by the 4
+//    waves through a double-buffered, XOR-swizzled LDS tile, loaded two or
+//    four chunks ahead.  WK waves split each 64-wide k-chunk when the weight
+//    dim is too short to give the chip enough work; their partial sums are
+//    added in LDS in a fixed order.
 //  * tiled (hundreds of rows per expert, weight dim not a multiple of 128):
 //    128 x 64 tiles with both operands double-buffered in LDS, 4 waves in a
 //    2 x 2 grid.
@@ -225,8 +225,10 @@ struct StreamShape {
   static constexpr int KC = 64;              // k per chunk (one LDS stage)
   static constexpr int KW = KC / WK;         // k per wave and chunk
   static constexpr int KSTEPS = KW / 16;     // MFMA k-steps per wave and chunk
-  // chunks in the weight ring: 16 KB in flight per wave (8 KB when a wave
-  // takes only 16 k of a chunk, to stay within the register budget)
+  // chunks in the weight ring: 16 KB in flight per wave at two workgroups
+  // per CU (8 KB when a wave takes only 16 k of a chunk, to stay within the
+  // register budget), 32 KB at one (8 chunks of one strip, 4 of two, 2 of
+  // four)
   static constexpr int PD = OCC == 1 ? (TN == 4 ? 2 : TN == 2 ? 4 : 8) : ((256 / KW) < 8 ? (256 / KW) : 8);
   // activation register slots: chunk c + AD is loaded while chunk c computes.
   // Loads complete in issue order, so the wait for chunk c + 1's activations
