@@ -188,6 +188,7 @@ __device__ __forceinline__ void copy_rows(const u32x4* __restrict__ x, void* __r
                                           const float* __restrict__ q_scale) {
   const int nv = NR * row_vecs;
   const float scale = q_scale ? *q_scale : 0.0f;
+  const float rscale = scale != 0.0f ? __fdiv_rn(1.0f, scale) : 0.0f;
   for (int j0 = threadIdx.x; j0 < nv; j0 += 256 * U) {
     u32x4 v[U];
     int64_t to[U];
@@ -205,7 +206,7 @@ __device__ __forceinline__ void copy_rows(const u32x4* __restrict__ x, void* __r
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (to[u] < 0) continue;
-      if (q_scale) ((uint2*)xd)[to[u]] = quantize8(v[u], scale);
+      if (q_scale) ((uint2*)xd)[to[u]] = quantize8(v[u], scale, rscale);
       else if (NT) __builtin_nontemporal_store(v[u], &((u32x4*)xd)[to[u]]);
       else ((u32x4*)xd)[to[u]] = v[u];
     }

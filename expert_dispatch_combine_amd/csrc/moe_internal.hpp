@@ -167,20 +167,40 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
-// eight bf16 (one 16-byte vector) -> eight E4M3 codes: code(bf16(x / scale));
-// a zero scale (all-zero activations) gives zero codes
-__device__ __forceinline__ uint2 quantize8(u32x4 v, float scale) {
-  uint32_t out[2] = {0u, 0u};
-  if (scale != 0.0f) {
+// bf16(x / scale) with x / scale the correctly rounded fp32 quotient, from
+// rscale = RN(1 / scale): the product x * rscale lies within 3 fp32 ulps of
+// the quotient, so it rounds to the same bf16 unless its low 16 bits are
+// within 4 of the bf16 rounding midpoint; only then is the quotient divided
+// out exactly.
+__device__ __forceinline__ float bf16_quotient(float x, float scale, float rscale) {
+  float q = x * rscale;
+  if ((__float_as_uint(q) & 0xFFFFu) - 0x7FFCu <= 8u) q = __fdiv_rn(x, scale);
+  const __bf16 hb = (__bf16)q;  // round to nearest even (gfx950's packed conversion)
+  return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// four E4M3 codes, a in the low byte: gfx950's packed conversion (round to
+// nearest even, the OCP E4M3 encoding; it equals e4m3_code on every bf16
+// value up to 464 in magnitude), e4m3_code beyond that range
+__device__ __forceinline__ uint32_t e4m3_code4(float a, float b, float c, float d) {
+  if (!(fabsf(a) <= 464.0f && fabsf(b) <= 464.0f && fabsf(c) <= 464.0f && fabsf(d) <= 464.0f))
+    return e4m3_code(a) | (e4m3_code(b) << 8) | (e4m3_code(c) << 16) | (e4m3_code(d) << 24);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// eight bf16 (one 16-byte vector) -> eight E4M3 codes: code(bf16(x / scale)),
+// rscale = RN(1 / scale); a zero scale (all-zero activations) gives zero codes
+__device__ __forceinline__ uint2 quantize8(u32x4 v, float scale, float rscale) {
+  if (scale == 0.0f) return make_uint2(0u, 0u);
+  float q[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t w = v[i >> 1];
-      const float x = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
-      const float q = __uint_as_float(bf16_rne_bits(__fdiv_rn(x, scale)) << 16);
-      out[i >> 2] |= e4m3_code(q) << (8 * (i & 3));
-    }
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w = v[i >> 1];
+    const float x = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    q[i] = bf16_quotient(x, scale, rscale);
   }
-  return make_uint2(out[0], out[1]);
+  return make_uint2(e4m3_code4(q[0], q[1], q[2], q[3]), e4m3_code4(q[4], q[5], q[6], q[7]));
 }
 
 // dst[row] = x[row_token[row]] for row < offsets[E] (rows of row_bytes bytes;

@@ -77,6 +77,36 @@ def test_fp8_scale_and_codes_random(T, h, mag):
     assert np.array_equal(xq[:R].cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("peak", [448.0, 300.0, 1e-3])
+def test_fp8_codes_of_every_bf16_value(peak):
+    """The activations hold every finite bf16 value with |v| <= peak (and
+    zeros to fill the last row): peak 448 makes the scale exactly 1, so every
+    bf16 value up to 448 meets the E4M3 encoding; 300 makes a scale of
+    0.66796875, so every pattern goes through the quotient by the scale and
+    its rounding to bf16; 1e-3 reaches the bf16 subnormals.  Every code
+    bit-exact against the oracle."""
+    banner(f"fp8 every bf16 value, peak {peak}")
+    pat = np.arange(0, 0x7F80, dtype=np.uint32)          # finite, non-negative bf16 patterns
+    vals = (pat << 16).view(np.float32)
+    pat = pat[np.abs(vals) <= peak].astype(np.uint16)
+    allp = np.concatenate([pat, pat | np.uint16(0x8000)])  # both signs
+    h = 256
+    T = (allp.size + h - 1) // h
+    pad = np.zeros(T * h, np.uint16)
+    pad[:allp.size] = allp
+    cfg = W.custom(T=T, h=h, E=2, K=1, F=64, cf=2.0, dtype="bf16", seed=11)
+    inp = custom_inputs(cfg, with_experts=False)
+    inp.x.copy_(torch.from_numpy(pad.view(np.int16).reshape(T, h)).view(torch.bfloat16).cuda())
+    x64 = host(inp.x)
+    assert float(np.abs(x64).max()) <= peak
+    idx = np.random.default_rng(int(peak * 7) % 1000).integers(0, 2, (T, 1)).astype(np.int32)
+    mc, b, scale, scale_v, xq = _fp8_dispatch(inp, idx, T)
+    assert scale_v == O.fp8_scale(x64)
+    sl = O.slot_routes(idx, 2, T)
+    want = O.fp8_quantize(x64[sl["row_token"]], scale_v)
+    assert np.array_equal(xq[:sl["R"]].cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("cid", [2, 5])
 def test_dispatch_fp8_on_workloads(cid):
     """Routing outputs equal the bf16 dispatch's (and the oracle's); codes of
