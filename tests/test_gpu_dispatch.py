@@ -91,7 +91,10 @@ def _random_idx(rng, T, E, K):
 
 @pytest.mark.parametrize("T,E,K,cf", [(1, 1, 1, 1.0), (3, 2, 2, 1.0), (300, 5, 2, 0.7),
                                       (1025, 8, 3, 1.0), (2049, 64, 6, 1.0), (777, 256, 8, 1.3),
-                                      (4000, 1000, 4, 1.0), (1500, 3, 1, 0.2), (64, 7, 7, 1.0)])
+                                      (4000, 1000, 4, 1.0), (1500, 3, 1, 0.2), (64, 7, 7, 1.0),
+                                      # the library's limits, E = 1024 and K = 32: one launch
+                                      # (6400 routes) and three kernels with drops (48000)
+                                      (200, 1024, 32, 1.0), (1500, 1024, 32, 0.5)])
 def test_dispatch_random_routings(T, E, K, cf):
     banner(f"dispatch random T={T} E={E} K={K} cf={cf}")
     rng = np.random.default_rng(T + E + K)

@@ -245,7 +245,10 @@ def _check_combine(T, K, h, R, drop_frac, seed):
                                           (2048, 1, 768, 2048, 0.0), (300, 8, 100, 2000, 0.3),
                                           (1000, 6, 2048, 3000, 0.5), (77, 3, 13, 50, 0.2),
                                           (40, 2, 4100, 60, 0.1), (33, 3, 6000, 80, 0.2),
-                                          (20, 8, 8192, 150, 0.0), (9, 4, 8196, 30, 0.3)])
+                                          (20, 8, 8192, 150, 0.0), (9, 4, 8196, 30, 0.3),
+                                          # K = 32, the library's limit: 16 tokens per
+                                          # workgroup (512 LDS entries) and one per workgroup
+                                          (50, 32, 256, 1500, 0.2), (3, 32, 7168, 90, 0.0)])
 def test_combine(T, K, h, R, drop):
     banner(f"combine T={T} K={K} h={h}")
     _check_combine(T, K, h, R, drop, seed=T + h)

@@ -71,7 +71,8 @@ def test_ledger_on_workloads(cid):
 
 @pytest.mark.parametrize("T,E,K,n_ep,cf", [(1, 1, 1, 1, 1.0), (300, 5, 2, 3, 0.7),
                                            (5000, 64, 6, 64, 1.0), (999, 1000, 4, 7, 1.0),
-                                           (4097, 256, 8, 8, 0.5)])
+                                           (4097, 256, 8, 8, 0.5),
+                                           (1500, 1024, 32, 64, 0.5)])  # E, K, n_ep at their limits
 def test_ledger_random(T, E, K, n_ep, cf):
     banner(f"ledger random T={T} E={E} K={K} n_ep={n_ep}")
     rng = np.random.default_rng(T + E)

@@ -48,7 +48,7 @@ def test_shared_logits_bit_exact(cid):
 
 @pytest.mark.parametrize("T,E,K", [(1, 1, 1), (17, 3, 2), (300, 4, 4), (129, 8, 8), (77, 33, 5),
                                    (513, 64, 6), (100, 100, 32), (64, 256, 8), (33, 1000, 3),
-                                   (70, 1024, 1), (257, 16, 16), (5, 5, 5)])
+                                   (70, 1024, 1), (257, 16, 16), (5, 5, 5), (64, 1024, 32)])
 def test_tie_heavy_integer_logits(T, E, K):
     banner(f"route ties T={T} E={E} K={K}")
     rng = np.random.default_rng(T * 131 + E)
@@ -132,6 +132,7 @@ def test_router_product_ragged_shapes(T, h, E, K):
     (130, 192, 1001, 4, True),     # eight expert tiles, odd E, h not splittable
     (1000, 448, 130, 3, True),     # E just above one 128-expert tile
     (90, 256, 100, 5, True),       # 64 x 128 tiles, 4 h ranges
+    (300, 512, 1024, 32, True),    # E = 1024 and K = 32, the library's limits
 ])
 def test_router_tiled_shapes(T, h, E, K, ws):
     """The tiled router product (long batches or E > 64) on shapes that
@@ -160,7 +161,9 @@ def test_router_tiled_shapes(T, h, E, K, ws):
     tie = near_tie_tokens(logits_o, bias, K)
     same = np.all(idx_g == idx_o, axis=1)
     assert np.all(same | tie), np.nonzero(~(same | tie))[0][:10]
-    assert tie.mean() < 0.05
+    # most tokens are compared: each of the K gaps among a token's top K + 1
+    # logits may fall under the tie threshold, so the excluded share grows with K
+    assert tie.mean() < 0.05 * max(1.0, K / 8)
     m = same & ~tie
     tol = 2.0 * float(err.max()) + 2 * GATE_RTOL
     np.testing.assert_allclose(gate_g[m], gate_o[m], rtol=tol, atol=1e-30)
