@@ -46,13 +46,18 @@
 //  * wide with weights in registers (packed weights, 512 or more rows per
 //    expert): 256 x 256 tiles, each wave all 256 rows x 64 weight rows of
 //    its own, its weight fragments loaded straight into registers; only the
-//    activations go through LDS.
+//    activations go through LDS.  An expert's last, partial row tile stages
+//    and multiplies only its 32-row sub-tiles that hold rows (2, 4 or 8),
+//    and each XCD runs those cheaper tiles after all its whole ones, so they
+//    fill the end of the launch.
 //
 // Scheduling is on the device (no host sync): every workgroup derives the
 // per-expert tile counts from `offsets`, maps its id to a logical tile with an
 // XCD-aware permutation (consecutive logical tiles run on the same XCD and
 // share its L2) and exits if it has none.  Logical tiles are ordered by
-// expert, then groups of 8 weight tiles, then row tiles fastest.  Where the
+// expert, then groups of 8 weight tiles, then row tiles fastest (the
+// weights-in-registers kernel takes the partial row tiles out of that order
+// and runs them last).  Where the
 // capacity fits one row tile of the streaming shape, every expert has one row
 // tile whatever the routing, so the map needs no `offsets` and the weight
 // prefetch starts before the expert's row range is read.
@@ -164,6 +169,68 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
           const int within = r - ng * nmt * NGROUP;
           const int mt = within % nmt;
           const int nt = ng * NGROUP + within / nmt;
+          sh->e = e;
+          sh->row0 = o0 + mt * BM;
+          sh->row_end = o1;
+          sh->n0 = nt * BN;
+        }
+        p += t;
+      }
+    }
+  }
+  __syncthreads();
+  return sh->e >= 0;
+}
+
+// The tile map of the weights-in-registers kernel.  Each XCD walks its share
+// of the experts' whole BM-row tiles first (in find_tile's order: expert,
+// groups of 8 weight tiles, row tiles fastest), then its share of the
+// experts' last, partial row tiles, which cost less (only their 32-row
+// sub-tiles that hold rows run MFMAs) and so fill the end of the launch.
+// Needs grid / NXCD >= ceil(TF / NXCD) + ceil(TP / NXCD) workgroups per XCD
+// (TF whole, TP partial tiles).
+template <int BM, int BN>
+__device__ __forceinline__ bool find_tile_partial_last(const int32_t* __restrict__ offsets,
+                                                       int E, int N, TileInfo* sh, int tid) {
+  const int ntn = (N + BN - 1) / BN;
+  if (tid < 64) {
+    const int lane = tid;
+    if (lane == 0) sh->e = -1;
+    const int per = (E + 63) / 64;
+    const int ebeg = min(E, lane * per), eend = min(E, ebeg + per);
+    int mf = 0, mp = 0;
+    for (int e = ebeg; e < eend; ++e) {
+      const int rows = offsets[e + 1] - offsets[e];
+      mf += rows / BM * ntn;
+      mp += (rows % BM != 0) ? ntn : 0;
+    }
+    const int incf = wave_incl_scan(mf), incp = wave_incl_scan(mp);
+    const int TF = __builtin_amdgcn_readlane(incf, 63), TP = __builtin_amdgcn_readlane(incp, 63);
+    const int pf = (TF + NXCD - 1) / NXCD, pp = (TP + NXCD - 1) / NXCD;
+    const int x = blockIdx.x % NXCD, j = blockIdx.x / NXCD;
+    const int nfx = max(0, min(pf, TF - x * pf)), npx = max(0, min(pp, TP - x * pp));
+    int L = -1;
+    const bool part = j >= nfx;
+    if (!part) L = x * pf + j;
+    else if (j - nfx < npx) L = x * pp + (j - nfx);
+    if (L >= 0) {
+      int p = part ? incp - mp : incf - mf;
+      for (int e = ebeg; e < eend; ++e) {
+        const int o0 = offsets[e], o1 = offsets[e + 1];
+        const int nfull = (o1 - o0) / BM;
+        const int t = part ? (((o1 - o0) % BM != 0) ? ntn : 0) : nfull * ntn;
+        if (L >= p && L < p + t) {
+          const int r = L - p;
+          int mt, nt;
+          if (part) {
+            mt = nfull;
+            nt = r;
+          } else {
+            const int ng = r / (nfull * NGROUP);
+            const int within = r - ng * nfull * NGROUP;
+            mt = within % nfull;
+            nt = ng * NGROUP + within / nfull;
+          }
           sh->e = e;
           sh->row0 = o0 + mt * BM;
           sh->row_end = o1;
@@ -906,21 +973,25 @@ __global__ __launch_bounds__(256, OCC) void wide_gemm_kernel(
 // chunk c is computed and staged after its MFMAs; one barrier per chunk.
 // The tile's weight rows beyond N (N % 256 != 0, N % 64 == 0) leave whole
 // waves idle but present at the barriers.
-template <int EPI, int AB>
-__global__ __launch_bounds__(256, 1) void wide2_gemm_kernel(
-    const void* __restrict__ A, const uint16_t* __restrict__ W,
-    const float* __restrict__ bias, void* __restrict__ out,
-    const int32_t* __restrict__ offsets, int E, int N, int Kd,
-    const int32_t* __restrict__ rowmap, const float* __restrict__ ascale) {
-  constexpr int BM = 256, BN = 256, TM = 8, TN = 2, PD = 3, AQ = BM * 8 / 256;
-  constexpr int STAGE = BM * 64;  // bf16 elements of one activation stage
+// TM = 32-row sub-tiles that hold rows (8 for a whole tile; a partial last
+// tile of up to 64 or 128 rows runs with 2 or 4: only those sub-tiles are
+// staged, read and multiplied).
+constexpr int W2_BM = 256, W2_BN = 256;
+constexpr int W2_STAGE = W2_BM * 64;  // bf16 elements of one activation stage
+
+template <int EPI, int AB, int TM>
+__device__ __forceinline__ void wide2_tile(const void* __restrict__ A,
+                                           const uint16_t* __restrict__ W,
+                                           const float* __restrict__ bias,
+                                           void* __restrict__ out, int N, int Kd,
+                                           const int32_t* __restrict__ rowmap,
+                                           const float* __restrict__ ascale, int e, int row0,
+                                           int row_end, int n0, uint16_t* act) {
+  constexpr int TN = 2, PD = 3, AQ = TM;  // AQ: activation quads per thread and chunk
+  constexpr int STAGE = W2_STAGE;
   using AI = ActIn<AB>;
   using AV = typename AI::V;
-  __shared__ __attribute__((aligned(16))) uint16_t act[2 * STAGE];
-  __shared__ TileInfo tinfo;
   const int tid = threadIdx.x;
-  if (!find_tile<BM, BN>(offsets, E, N, &tinfo, tid)) return;
-  const int e = tinfo.e, row0 = tinfo.row0, row_end = tinfo.row_end, n0 = tinfo.n0;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, lg = lane >> 5;
   const int nk = Kd / 64;
@@ -1046,6 +1117,25 @@ __global__ __launch_bounds__(256, 1) void wide2_gemm_kernel(
     for (int tn = 0; tn < TN; ++tn)
       store_tile<EPI>(acc[tm][tn], bptr, out, m, ncol + tn * 32 + lg * 4, N);
   }
+}
+
+template <int EPI, int AB>
+__global__ __launch_bounds__(256, 1) void wide2_gemm_kernel(
+    const void* __restrict__ A, const uint16_t* __restrict__ W,
+    const float* __restrict__ bias, void* __restrict__ out,
+    const int32_t* __restrict__ offsets, int E, int N, int Kd,
+    const int32_t* __restrict__ rowmap, const float* __restrict__ ascale) {
+  __shared__ __attribute__((aligned(16))) uint16_t act[2 * W2_STAGE];
+  __shared__ TileInfo tinfo;
+  if (!find_tile_partial_last<W2_BM, W2_BN>(offsets, E, N, &tinfo, threadIdx.x)) return;
+  const int e = tinfo.e, row0 = tinfo.row0, row_end = tinfo.row_end, n0 = tinfo.n0;
+  const int rows = __builtin_amdgcn_readfirstlane(min(W2_BM, row_end - row0));
+  if (rows > 128)
+    wide2_tile<EPI, AB, 8>(A, W, bias, out, N, Kd, rowmap, ascale, e, row0, row_end, n0, act);
+  else if (rows > 64)
+    wide2_tile<EPI, AB, 4>(A, W, bias, out, N, Kd, rowmap, ascale, e, row0, row_end, n0, act);
+  else
+    wide2_tile<EPI, AB, 2>(A, W, bias, out, N, Kd, rowmap, ascale, e, row0, row_end, n0, act);
 }
 
 // ==========================================================================
@@ -1184,7 +1274,9 @@ hipError_t launch_wide(const GemmArgs& g) {
 
 template <int EPI, int AB>
 hipError_t launch_wide2(const GemmArgs& g) {
-  const int64_t grid = grid_for(g.r_max, 256, g.E, g.N, 256);
+  // whole and partial tiles are split over the XCDs separately, which can
+  // take one workgroup per XCD more than their sum
+  const int64_t grid = grid_for(g.r_max, W2_BM, g.E, g.N, W2_BN) + NXCD;
   hipLaunchKernelGGL((wide2_gemm_kernel<EPI, AB>), dim3((unsigned)grid), dim3(256), 0, g.s, g.A,
                      g.W, g.bias, g.out, g.offsets, g.E, g.N, g.Kd, g.rowmap, g.ascale);
   return hipGetLastError();

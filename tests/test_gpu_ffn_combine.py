@@ -160,6 +160,27 @@ def test_ffn_static_map_with_empty_experts(packed):
     _check_rows(inp, sl, b, np.arange(sl["R"]))
 
 
+def test_ffn_partial_row_tiles_of_every_size():
+    """Weights in registers (packed weights, 521 rows per expert on average):
+    experts whose last 256-row tile holds 1, 31, 32, 33, 64, 65, 128, 129,
+    255, 256 (none) or 257 (one whole tile and 1) rows, and one of 5000 rows
+    (19 whole tiles and 136): the partial tiles run with 2, 4 or 8 of their
+    32-row sub-tiles, after each XCD's whole tiles; F = 384 leaves half of
+    the first GEMM's second weight tile idle.  Every row against the oracle."""
+    banner("ffn partial row tiles of every size")
+    sizes = [1, 31, 32, 33, 64, 65, 128, 129, 255, 256, 257, 5000]
+    E, T = len(sizes), sum(sizes)
+    cfg = W.custom(T=T, h=256, E=E, K=1, F=384, cf=10.0, dtype="bf16", seed=91)
+    inp = custom_inputs(cfg)
+    rng = np.random.default_rng(91)
+    idx = rng.permutation(np.repeat(np.arange(E), sizes)).astype(np.int32)[:, None]
+    cap = O.capacity(T, E, cfg.cf)
+    sl = O.slot_routes(idx, E, cap)
+    assert np.array_equal(np.diff(sl["expert_offsets"]), sizes)
+    b = _run_ffn(inp, cap, sl, packed=True)
+    _check_rows(inp, sl, b, np.arange(sl["R"]))
+
+
 @pytest.mark.parametrize("cid,shape,packed", [
     (2, None, True), (2, None, False),                     # gather in the streaming loads
     (None, (2048, 768, 14, 1, 3072, 1.0), True),           # ragged, static tile map
