@@ -25,6 +25,8 @@ namespace {
 
 constexpr int RPB = kDispatchRoutesPerBlock;  // routes per block
 constexpr int CHUNK = 256;                    // routes per pass (one per thread)
+constexpr int NPASS = RPB / CHUNK;            // passes of the slot kernel
+constexpr int COL_LOADS = 32;                 // count-matrix loads in flight per thread
 
 __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ idx,
                                                     int64_t A, int E,
@@ -99,19 +101,36 @@ __global__ __launch_bounds__(256) void slot_kernel(
   __shared__ int sh_wave[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
+  const int64_t base = (int64_t)b * RPB;
+  // this block's expert ids, loaded first so that they arrive during step 1
+  int ids[NPASS];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const int64_t i = base + p * CHUNK + tid;
+    ids[p] = i < A ? idx[i] : -1;
+  }
 
   // 1. per expert: routes in earlier blocks (-> run) and in all blocks (load)
   //    -> accepted = min(load, cap) -> exclusive scan over experts (-> off).
-  //    S threads share one expert's column of the count matrix.
+  //    S threads share one expert's column of the count matrix.  The counts
+  //    were written by other XCDs, so each round trip is a full memory
+  //    latency: up to 32 loads per thread are issued before their sums.
   const int S = (E >= 256) ? 1 : (256 / E);
   for (int w = tid; w < E * S; w += 256) {
     const int e = w % E, sl = w / E;
     int bef = 0, tot = 0;
-#pragma unroll 4
-    for (int bb = sl; bb < nblocks; bb += S) {
-      const int c = counts[(size_t)bb * (E + 1) + e];
-      tot += c;
-      bef += (bb < b) ? c : 0;
+    for (int bb0 = sl; bb0 < nblocks; bb0 += COL_LOADS * S) {
+      int c[COL_LOADS];
+#pragma unroll
+      for (int u = 0; u < COL_LOADS; ++u) {
+        const int bb = bb0 + u * S;
+        c[u] = bb < nblocks ? counts[(size_t)bb * (E + 1) + e] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < COL_LOADS; ++u) {
+        tot += c[u];
+        bef += (bb0 + u * S < b) ? c[u] : 0;
+      }
     }
     ptot[w] = tot;
     pbef[w] = bef;
@@ -136,11 +155,10 @@ __global__ __launch_bounds__(256) void slot_kernel(
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int64_t base = (int64_t)b * RPB;
-  for (int p = 0; p < RPB / CHUNK; ++p) {
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
     const int64_t i = base + p * CHUNK + tid;
-    int id = -1;
-    if (i < A) id = idx[i];
+    const int id = ids[p];
     const bool valid = (i < A) && id >= 0 && id < E;
     for (int e = tid; e < 4 * E; e += 256) (&wcnt[0][0])[e / E * kMaxExperts + e % E] = 0;
     __syncthreads();
@@ -238,6 +256,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
 // The whole dispatch for A <= kSmallDispatchRoutes in one launch; block b
 // owns routes [16b, 16b + 16).
 constexpr int SBR = 16;
+constexpr int SBL = 8;  // route ids loaded per thread at once
 __global__ __launch_bounds__(256) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, int A, int K, int E, int64_t cap,
     const u32x4* __restrict__ x, int row_vecs, int32_t* __restrict__ offsets,
@@ -252,20 +271,20 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
   for (int e = tid; e < E; e += 256) tot[e] = bef[e] = 0;
   __syncthreads();
   // all routes: totals, and the routes before this block (the stable order).
-  // Eight loads per thread in flight; lanes of a wave with the same expert
+  // SBL loads per thread in flight; lanes of a wave with the same expert
   // are found with ballots on the id bits, and one of them adds their count.
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int i0 = 0; i0 < A; i0 += 256 * 8) {
-    int ids[8];
+  for (int i0 = 0; i0 < A; i0 += 256 * SBL) {
+    int ids[SBL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < SBL; ++u) {
       const int i = i0 + u * 256 + tid;
       ids[u] = i < A ? idx[i] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < SBL; ++u) {
       const int i = i0 + u * 256 + tid;
       const int id = ids[u];
       if (i >= base && i < base + SBR) own_id[i - base] = id;  // this block's routes

@@ -94,6 +94,35 @@ __device__ __forceinline__ float topk_gate(float slot_v, float vmax, int gl, int
   return w / group_sum<G>(w);
 }
 
+// Most h ranges a router product is split into (the top-k kernels add the
+// partial products of at most this many ranges).
+constexpr int kMaxRouterSplit = 8;
+
+// Logits e_j = gl + j*G (j < VMAX, e_j < E) of one token from the KS partial
+// products at pt[e + k * pstride], added in range order.  Every load is
+// issued before the first addition: the partials were just written by other
+// XCDs, so each dependent load would cost a full memory round trip.  Ranges
+// k >= KS re-read range KS - 1 (a cache hit) and are not added; lanes past E
+// read logit E - 1 and discard it.
+template <int VMAX, int G>
+__device__ __forceinline__ void sum_parts(const float* __restrict__ pt, int KS, int64_t pstride,
+                                          int gl, int E, float (&v)[VMAX]) {
+  float p[VMAX][kMaxRouterSplit];
+#pragma unroll
+  for (int j = 0; j < VMAX; ++j) {
+    const int e = min(gl + j * G, E - 1);
+#pragma unroll
+    for (int k = 0; k < kMaxRouterSplit; ++k) p[j][k] = pt[e + min(k, KS - 1) * pstride];
+  }
+#pragma unroll
+  for (int j = 0; j < VMAX; ++j) {
+    v[j] = p[j][0];
+#pragma unroll
+    for (int k = 1; k < kMaxRouterSplit; ++k)
+      if (k < KS) v[j] += p[j][k];
+  }
+}
+
 // --------------------------------------------------------------------------
 // Standalone top-k kernel over fp32 logits in global memory.  With `parts`
 // the logits are first formed as the sum of KS partial products over
@@ -122,15 +151,15 @@ __global__ __launch_bounds__(256) void topk_kernel(float* __restrict__ logits,
   for (int t = t_begin + grp; t < t_end; t += GPB) {
     float val[VMAX];
     float* row = logits + (size_t)t * E;
+    float ps[VMAX];
+    if (parts) sum_parts<VMAX, G>(parts + (size_t)t * E, KS, pstride, gl, E, ps);
 #pragma unroll
     for (int j = 0; j < VMAX; ++j) {
       const int e = gl + j * G;
       float v = -INFINITY;
       if (e < E) {
         if (parts) {
-          const float* pr = parts + (size_t)t * E + e;
-          v = pr[0];
-          for (int k2 = 1; k2 < KS; ++k2) v += pr[k2 * pstride];
+          v = ps[j];
           row[e] = v;
         } else {
           v = row[e];
@@ -194,6 +223,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(float* __restrict__ lo
   const bool valid = t < T;  // uniform per wave; idle waves still reach the barrier
   // keys; 0 (below every finite value and -inf) pads lanes past E
   uint32_t key[VMAX];
+  float ps[VMAX];
+  if (valid && parts) sum_parts<VMAX, 64>(parts + (size_t)t * E, KS, pstride, lane, E, ps);
 #pragma unroll
   for (int j = 0; j < VMAX; ++j) {
     const int e = lane + 64 * j;
@@ -202,9 +233,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(float* __restrict__ lo
       float* row = logits + (size_t)t * E;
       float v;
       if (parts) {
-        const float* pr = parts + (size_t)t * E + e;
-        v = pr[0];
-        for (int k2 = 1; k2 < KS; ++k2) v += pr[k2 * pstride];
+        v = ps[j];
         row[e] = v;
       } else {
         v = row[e];
@@ -772,7 +801,7 @@ RouterPlan router_plan(int T, int h, int E, int K, size_t parts_room) {
   const int64_t tiles = (int64_t)((T + p.tt - 1) / p.tt) * ((E + p.ee - 1) / p.ee);
   // split h while the launch still fits one workgroup per CU (256 CUs)
   p.ks = 1;
-  while (p.ks < 8 && tiles * p.ks * 2 <= 256 && (h / 64) % (p.ks * 2) == 0 &&
+  while (p.ks < kMaxRouterSplit && tiles * p.ks * 2 <= 256 && (h / 64) % (p.ks * 2) == 0 &&
          (size_t)(p.ks * 2) * T * E * sizeof(float) <= parts_room)
     p.ks *= 2;
   p.fuse = p.ks == 1 && E <= p.ee && K <= 16;
