@@ -94,7 +94,10 @@ def _random_idx(rng, T, E, K):
                                       (4000, 1000, 4, 1.0), (1500, 3, 1, 0.2), (64, 7, 7, 1.0),
                                       # the library's limits, E = 1024 and K = 32: one launch
                                       # (6400 routes) and three kernels with drops (48000)
-                                      (200, 1024, 32, 1.0), (1500, 1024, 32, 0.5)])
+                                      (200, 1024, 32, 1.0), (1500, 1024, 32, 0.5),
+                                      # 141 route blocks at E = 64: each of an expert's four
+                                      # column readers sums its blocks in two batches
+                                      (24000, 64, 6, 1.0)])
 def test_dispatch_random_routings(T, E, K, cf):
     banner(f"dispatch random T={T} E={E} K={K} cf={cf}")
     rng = np.random.default_rng(T + E + K)
