@@ -194,10 +194,15 @@ __global__ __launch_bounds__(256) void slot_kernel(
 }
 
 // Copy NR token rows: xd[dst[r]] = x[src[r]] for r < NR with dst[r] >= 0
-// (row indices, in LDS).  The NR * row_vecs 16-byte vectors are spread over
-// the 256 threads; each thread issues U loads before their stores.  With a
-// scale (FP8 payload) each 16-byte vector of eight bf16 becomes eight E4M3
-// codes (8 bytes) of the destination row.
+// (row indices, in LDS; every src[r] is a valid token, also where dst[r] < 0).
+// The NR * row_vecs 16-byte vectors are spread over the 256 threads; each
+// thread issues U loads before their stores.  The loads are unconditional
+// (positions past the last vector re-read it, rows without a destination
+// read their source row and are not stored): loads under a per-lane
+// condition had the compiler wait for each before it issued the next, one
+// memory round trip per vector.  With a scale (FP8 payload) each 16-byte
+// vector of eight bf16 becomes eight E4M3 codes (8 bytes) of the
+// destination row.
 // NT: nontemporal stores of the dispatched rows (chosen when they outgrow the
 // 256 MB last-level cache, which could not keep them for the expert GEMM).
 template <int NR, int U, bool NT = false>
@@ -212,14 +217,11 @@ __device__ __forceinline__ void copy_rows(const u32x4* __restrict__ x, void* __r
     int64_t to[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * 256;
+      const int j = min(j0 + u * 256, nv - 1);
       const int r = j / row_vecs;
       const int c = j - r * row_vecs;
-      to[u] = -1;
-      if (j < nv && dst[r] >= 0) {
-        v[u] = x[(int64_t)src[r] * row_vecs + c];
-        to[u] = (int64_t)dst[r] * row_vecs + c;
-      }
+      v[u] = x[(int64_t)src[r] * row_vecs + c];
+      to[u] = (j0 + u * 256 < nv && dst[r] >= 0) ? (int64_t)dst[r] * row_vecs + c : -1;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(
     }
     if (lane < SBR) {
       dst[lane] = row;
-      src[lane] = i / K;
+      src[lane] = i < A ? i / K : 0;  // a valid token also past the last route
     }
   }
   if (!xd) return;  // routing metadata only (uniform)
