@@ -36,11 +36,15 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
   for (int e = tid; e <= E; e += 256) hist[e] = 0;
   __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * RPB;
+  // all of this thread's ids are loaded before the first is counted (a load
+  // under the bounds check, counted at once, would cost a round trip each)
+  int ids[NPASS];
 #pragma unroll
-  for (int j = 0; j < RPB / 256; ++j) {
-    const int64_t i = base + j * 256 + tid;
-    if (i < A) {
-      const int id = idx[i];
+  for (int j = 0; j < NPASS; ++j) ids[j] = idx[min(base + j * 256 + tid, A - 1)];
+#pragma unroll
+  for (int j = 0; j < NPASS; ++j) {
+    if (base + j * 256 + tid < A) {
+      const int id = ids[j];
       const int bin = (id >= 0 && id < E) ? id : E;  // bin E: invalid ids
       atomicAdd(&hist[bin], 1);
     }

@@ -123,6 +123,17 @@ __device__ __forceinline__ void sum_parts(const float* __restrict__ pt, int KS, 
   }
 }
 
+// Logit biases of this lane's experts e_j = gl + j*G (lanes past E read
+// bias[E - 1] and never use it), every load issued before the first is used:
+// a bias read where it is added would cost a memory round trip per expert
+// and per token.
+template <int VMAX, int G>
+__device__ __forceinline__ void lane_bias(const float* __restrict__ bias, int gl, int E,
+                                          float (&b)[VMAX]) {
+#pragma unroll
+  for (int j = 0; j < VMAX; ++j) b[j] = bias[min(gl + j * G, E - 1)];
+}
+
 // --------------------------------------------------------------------------
 // Standalone top-k kernel over fp32 logits in global memory.  With `parts`
 // the logits are first formed as the sum of KS partial products over
@@ -148,6 +159,8 @@ __global__ __launch_bounds__(256) void topk_kernel(float* __restrict__ logits,
   }
   const int t_begin = blockIdx.x * tokens_per_block;
   const int t_end = min(T, t_begin + tokens_per_block);
+  float bv[VMAX];
+  if (bias) lane_bias<VMAX, G>(bias, gl, E, bv);
   for (int t = t_begin + grp; t < t_end; t += GPB) {
     float val[VMAX];
     float* row = logits + (size_t)t * E;
@@ -164,7 +177,7 @@ __global__ __launch_bounds__(256) void topk_kernel(float* __restrict__ logits,
         } else {
           v = row[e];
         }
-        if (bias) v = v + bias[e];
+        if (bias) v = v + bv[j];
       }
       val[j] = v;
     }
@@ -223,7 +236,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(float* __restrict__ lo
   const bool valid = t < T;  // uniform per wave; idle waves still reach the barrier
   // keys; 0 (below every finite value and -inf) pads lanes past E
   uint32_t key[VMAX];
-  float ps[VMAX];
+  float ps[VMAX], bv[VMAX];
+  if (valid && bias) lane_bias<VMAX, 64>(bias, lane, E, bv);
   if (valid && parts) sum_parts<VMAX, 64>(parts + (size_t)t * E, KS, pstride, lane, E, ps);
 #pragma unroll
   for (int j = 0; j < VMAX; ++j) {
@@ -238,7 +252,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(float* __restrict__ lo
       } else {
         v = row[e];
       }
-      if (bias) v = v + bias[e];
+      if (bias) v = v + bv[j];
       k = order_key(v);
     }
     key[j] = k;
@@ -395,6 +409,8 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   const int gl = tid % G;
   const int tt = tid / G;
   const int t = t0 + tt;
+  float bv[VMAX];
+  if (bias) lane_bias<VMAX, G>(bias, gl, E, bv);
   float val[VMAX];
 #pragma unroll
   for (int j = 0; j < VMAX; ++j) {
@@ -402,7 +418,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     float v = -INFINITY;
     if (e < E) {
       v = tile[tt][e];
-      if (bias) v = v + bias[e];
+      if (bias) v = v + bv[j];
     }
     val[j] = v;
   }
@@ -467,6 +483,8 @@ __device__ __forceinline__ void tile_topk(const float* tile, const float* __rest
   static_assert(VMAX <= 32, "one bit per slot of the taken mask");
   const int tid = threadIdx.x;
   const int gl = tid % G;
+  float bv[VMAX];
+  if (bias) lane_bias<VMAX, G>(bias, gl, E, bv);
   for (int p = 0; p < TT / (256 / G); ++p) {
     const int tl = p * (256 / G) + tid / G;
     const int t = t0 + tl;
@@ -477,7 +495,7 @@ __device__ __forceinline__ void tile_topk(const float* tile, const float* __rest
       float v = -INFINITY;
       if (e < E) {
         v = tile[tl * PITCH + e];
-        if (bias) v = v + bias[e];
+        if (bias) v = v + bv[j];
       }
       val[j] = v;
     }
