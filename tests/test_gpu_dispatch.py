@@ -20,6 +20,7 @@ def _dispatch(cfg: W.Config, x: torch.Tensor, idx: np.ndarray, cap: int):
     b = LayerBuffers(mc, cap)
     b.topk_idx.copy_(torch.from_numpy(idx.astype(np.int32)))
     b.row_token.fill_(-7)
+    b.x_disp.view(torch.uint8).fill_(0x5A)  # rows past R must keep this
     M.moe_dispatch(mc, x, b.topk_idx, cap, b.expert_offsets, b.route_rank, b.route_row,
                    b.row_token, b.x_disp, b.expert_load, b.ws)
     torch.cuda.synchronize()
@@ -42,6 +43,9 @@ def _check(cfg, x, idx, cap, check_rows=True):
         xd_o = O.dispatch(x.cpu().view(bits).numpy(), sl["row_token"])
         got = b.x_disp[:R].cpu().view(bits).numpy()
         assert np.array_equal(got, xd_o)
+    if check_rows:
+        # the row copy loads every vector position but stores accepted rows only
+        assert bool((b.x_disp[R:].view(torch.uint8) == 0x5A).all())
     return b, sl
 
 
