@@ -204,7 +204,8 @@ int moe_bias_update(const moe_cfg* cfg, const int32_t* topk_idx, float* expert_b
  *   route_row      [T,K] int32   offset[e] + rank if rank < capacity, else -1
  *   row_token      [R_max] int32 token of each accepted row (rows >= R are
  *                                left untouched)
- *   x_disp         [R_max, h] dtype  x_disp[row] = x[row_token[row]]; or NULL:
+ *   x_disp         [R_max, h] dtype  x_disp[row] = x[row_token[row]] (rows
+ *                                    >= R are left untouched); or NULL:
  *                                    routing metadata only (x may then be
  *                                    NULL), for moe_expert_ffn_rows
  *   expert_load    [E] int32|NULL    pre-capacity load of each expert
