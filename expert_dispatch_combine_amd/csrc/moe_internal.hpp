@@ -167,40 +167,54 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
-// bf16(x / scale) with x / scale the correctly rounded fp32 quotient, from
-// rscale = RN(1 / scale): the product x * rscale lies within 3 fp32 ulps of
-// the quotient, so it rounds to the same bf16 unless its low 16 bits are
-// within 4 of the bf16 rounding midpoint; only then is the quotient divided
-// out exactly.
-__device__ __forceinline__ float bf16_quotient(float x, float scale, float rscale) {
-  float q = x * rscale;
-  if ((__float_as_uint(q) & 0xFFFFu) - 0x7FFCu <= 8u) q = __fdiv_rn(x, scale);
-  const __bf16 hb = (__bf16)q;  // round to nearest even (gfx950's packed conversion)
-  return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
-
-// four E4M3 codes, a in the low byte: gfx950's packed conversion (round to
-// nearest even, the OCP E4M3 encoding; it equals e4m3_code on every bf16
-// value up to 464 in magnitude), e4m3_code beyond that range
-__device__ __forceinline__ uint32_t e4m3_code4(float a, float b, float c, float d) {
-  if (!(fabsf(a) <= 464.0f && fabsf(b) <= 464.0f && fabsf(c) <= 464.0f && fabsf(d) <= 464.0f))
-    return e4m3_code(a) | (e4m3_code(b) << 8) | (e4m3_code(c) << 16) | (e4m3_code(d) << 24);
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-}
-
 // eight bf16 (one 16-byte vector) -> eight E4M3 codes: code(bf16(x / scale)),
-// rscale = RN(1 / scale); a zero scale (all-zero activations) gives zero codes
+// rscale = RN(1 / scale); a zero scale (all-zero activations) gives zero codes.
+// bf16(x / scale) with x / scale the correctly rounded fp32 quotient: the
+// product x * rscale lies within 3 fp32 ulps of the quotient, so it rounds to
+// the same bf16 unless its low 16 bits are within 4 of the bf16 rounding
+// midpoint; only then is the quotient divided out exactly.  The codes come
+// from gfx950's packed conversion (round to nearest even, the OCP E4M3
+// encoding; it equals e4m3_code on every bf16 value up to 464 in magnitude),
+// from e4m3_code beyond that range.  Both rare cases are tested once per
+// vector, so the common path has no branch.
 __device__ __forceinline__ uint2 quantize8(u32x4 v, float scale, float rscale) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x2v_ __attribute__((ext_vector_type(2)));
   if (scale == 0.0f) return make_uint2(0u, 0u);
-  float q[8];
+  float x[8], q[8];
+  bool near = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t w = v[i >> 1];
-    const float x = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
-    q[i] = bf16_quotient(x, scale, rscale);
+    x[i] = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    q[i] = x[i] * rscale;
+    near |= (__float_as_uint(q[i]) & 0xFFFFu) - 0x7FFCu <= 8u;
   }
-  return make_uint2(e4m3_code4(q[0], q[1], q[2], q[3]), e4m3_code4(q[4], q[5], q[6], q[7]));
+  if (near) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((__float_as_uint(q[i]) & 0xFFFFu) - 0x7FFCu <= 8u) q[i] = __fdiv_rn(x[i], scale);
+  }
+  // bf16 rounding (nearest even, packed conversion), widened back to fp32
+  float b[8];
+  bool in_range = true;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const uint32_t p = __builtin_bit_cast(
+        uint32_t, __builtin_convertvector(f32x2v_{q[i], q[i + 1]}, bf16x2v));
+    b[i] = __uint_as_float(p << 16);
+    b[i + 1] = __uint_as_float(p & 0xFFFF0000u);
+    in_range = in_range & (fabsf(b[i]) <= 464.0f) & (fabsf(b[i + 1]) <= 464.0f);
+  }
+  if (!in_range)
+    return make_uint2(e4m3_code(b[0]) | (e4m3_code(b[1]) << 8) | (e4m3_code(b[2]) << 16) |
+                          (e4m3_code(b[3]) << 24),
+                      e4m3_code(b[4]) | (e4m3_code(b[5]) << 8) | (e4m3_code(b[6]) << 16) |
+                          (e4m3_code(b[7]) << 24));
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(b[0], b[1], 0, false);
+  const int hi = __builtin_amdgcn_cvt_pk_fp8_f32(b[4], b[5], 0, false);
+  return make_uint2((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(b[2], b[3], lo, true),
+                    (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(b[6], b[7], hi, true));
 }
 
 // dst[row] = x[row_token[row]] for row < offsets[E] (rows of row_bytes bytes;
