@@ -77,6 +77,34 @@ def test_fp8_scale_and_codes_random(T, h, mag):
     assert np.array_equal(xq[:R].cpu().numpy(), want)
 
 
+def test_fp8_codes_beyond_the_format_with_a_caller_scale():
+    """A caller-supplied scale four times below max|x| / 448: within one
+    16-byte vector some quotients exceed the E4M3 range (NaN code beyond 464,
+    448 up to it) and others do not, so the quantiser's out-of-range path and
+    its ordinary path meet in the same vectors; every code bit-exact."""
+    banner("fp8 caller scale below the amax")
+    T, h = 300, 256
+    cfg = W.custom(T=T, h=h, E=2, K=1, F=64, cf=2.0, dtype="bf16", seed=41)
+    inp = custom_inputs(cfg, with_experts=False)
+    x64 = host(inp.x)
+    scale_v = O.fp8_scale(x64) / 4.0  # a power-of-two factor: still a bf16 value
+    assert scale_v > 0.0 and np.abs(x64 / scale_v).max() > 464.0
+    idx = np.random.default_rng(41).integers(0, 2, (T, 1)).astype(np.int32)
+    mc = _mc(cfg)
+    b = LayerBuffers(mc, T)
+    ws = torch.empty((M.moe_workspace_bytes(mc),), dtype=torch.uint8, device="cuda")
+    scale = torch.tensor([scale_v], dtype=torch.float32, device="cuda")
+    xq = torch.full((max(M.moe_max_rows(mc, T), 1), h), 0xAB, dtype=torch.uint8, device="cuda")
+    M.moe_dispatch_fp8(mc, inp.x, scale, torch.from_numpy(idx).cuda(), T, b.expert_offsets,
+                       b.route_rank, b.route_row, b.row_token, xq, b.expert_load, ws)
+    torch.cuda.synchronize()
+    sl = O.slot_routes(idx, 2, T)
+    R = sl["R"]
+    want = O.fp8_quantize(x64[sl["row_token"]], scale_v)
+    assert np.any((want & 0x7F) == 0x7F) and np.any((want & 0x7F) < 0x7F)
+    assert np.array_equal(xq[:R].cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("peak", [448.0, 300.0, 1e-3])
 def test_fp8_codes_of_every_bf16_value(peak):
     """The activations hold every finite bf16 value with |v| <= peak (and
